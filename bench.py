@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Absorbed-MLA decode benchmark on one MI355X.
+
+Workload: the DeepSeek-V2/V3-shaped decode layer, h=128, d_c=512, d_rope=64,
+d_qk_nope=d_v=128, batch 32, 4096 cached tokens + 1 query token per sequence
+(kv_len 4097), bf16 latent cache [32, 4097, 576], fp32 accumulation, seeded
+synthetic inputs. One step = one mla_decode call: query absorption + RoPE,
+split-K attention over the latent cache, split combine + W_UV up-projection.
+
+Prints one JSON line. Inputs are resident in HBM before the timed region. Three
+copies of (cache, packed weights) are used in turn, as three layers would be,
+so the 256 MB Infinity Cache cannot hold the working set between steps.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # dense bf16 matrix-core peak (256 CU x 2.4 GHz x 4096)
+COPIES = 3
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw hipEvent_t pairs (the library records them around its attention kernel,
+    on the stream that kernel is launched on)."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.pairs = []
+        for _ in range(n):
+            a, b = ctypes.c_void_p(), ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(a)) == 0
+            assert self.hip.hipEventCreate(ctypes.byref(b)) == 0
+            self.pairs.append((a.value, b.value))
+
+    def elapsed_ms(self, k):
+        ms = ctypes.c_float()
+        a, b = self.pairs[k]
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+
+def algorithmic(w):
+    """FLOPs and bytes the absorbed method needs per step (the cache read once,
+    the weights once, queries in, outputs out)."""
+    import numpy as np
+    kv = w.kv_lens.astype(np.float64)
+    vis = sum(float(n) - w.n_q + j + 1 for n in kv for j in range(w.n_q))
+    M = w.batch * w.n_q
+    flops = (2.0 * w.h * vis * (w.d_c + w.d_r) + 2.0 * w.h * vis * w.d_c
+             + 2.0 * w.h * M * w.d_n * w.d_c + 2.0 * w.h * M * w.d_c * w.d_v)
+    cache_bytes = float(kv.sum()) * (w.d_c + w.d_r) * 2
+    weight_bytes = 2.0 * w.d_c * w.h * (w.d_n + w.d_v)
+    io_bytes = M * w.h * (w.d_n + w.d_r) * 2 + M * w.h * w.d_v * 4
+    return flops, cache_bytes, cache_bytes + weight_bytes + io_bytes
+
+
+def kernel_source_hash():
+    p = os.path.join(ROOT, "mla_latent_kv_41_amd", "csrc", "decode_bf16.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()
+
+
+def traffic_from_profile(per_launch_units):
+    """HBM bytes per attention launch from the committed rocprofv3 counter runs,
+    or None when absent or taken on a different kernel source."""
+    p = os.path.join(ROOT, "profiles", "attention_traffic.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(w, t, budget_s=12.0):
+    """The fp64 oracle (explicit K/V, as it stands) on whole sequences of the same
+    workload until about budget_s of CPU time, scaled to TFLOP/s of the absorbed
+    method's algorithmic FLOPs for that sample."""
+    import numpy as np
+    import oracle
+    done, t0 = 0, time.perf_counter()
+    while done < w.batch and time.perf_counter() - t0 < budget_s:
+        sel = [(done, i) for i in range(w.h)]
+        oracle.mla_decode(h=w.h, d_c=w.d_c, d_r=w.d_r, d_n=w.d_n, d_v=w.d_v, c_kv=t["c_kv"],
+                          k_r=t["k_r"], kv_lens=w.kv_lens, q_nope=t["q_nope"], q_r=t["q_r"],
+                          w_uk=t["w_uk"], w_uv=t["w_uv"], store_bf16=True, select=sel)
+        done += 1
+    secs = time.perf_counter() - t0
+    flops, _, _ = algorithmic(w)
+    frac = done / w.batch
+    return {"value": flops * frac / secs / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": "%d of %d sequences (all %d heads), fp64 explicit-K/V oracle, %.1f s; "
+                      "query tokens/s %.3g" % (done, w.batch, w.h, secs, done * w.n_q / secs)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one 512 MiB device copy first (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from mla_latent_kv_41_amd import mla, synth
+    from mla_latent_kv_41_amd.harness import GpuStep
+
+    w = synth.make_workload(2)
+    t = synth.draw(w)
+    log("workload %s: B=%d kv_len=%d h=%d row=%d" % (w.name, w.batch, w.kv_max, w.h, w.row))
+    steps = [GpuStep(w, t, poison=False) for _ in range(COPIES)]
+    for s in steps[1:]:
+        s.q_nope, s.q_rope, s.out, s.lse = steps[0].q_nope, steps[0].q_rope, steps[0].out, steps[0].lse
+    torch.cuda.synchronize()
+
+    if args.calibrate_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    ev = HipEvents(args.steps)
+    for k in range(args.warmup):
+        steps[k % COPIES].decode()
+    torch.cuda.synchronize()
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for k in range(args.steps):
+        steps[k % COPIES].decode(events=ev.pairs[k])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms = total_ms / args.steps
+    attn_ms = [ev.elapsed_ms(k) for k in range(args.steps)]
+    attn_avg = float(np.mean(attn_ms))
+
+    flops, cache_bytes, alg_bytes = algorithmic(w)
+    tflops = flops / (ms * 1e-3) / 1e12
+    cache_gbps = cache_bytes / (ms * 1e-3) / 1e9
+    tok_s = w.batch * w.n_q / (ms * 1e-3)
+    attn_gbps = cache_bytes / (attn_avg * 1e-3) / 1e9
+    traffic = traffic_from_profile(1)
+    out = {
+        "metric": "MLA decode TFLOP/s + latent-cache GB/s (% roofline), h=128 B=32 ctx=4096",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; N(0,1) RMS-normalised latents, N(0,1/512) weights)",
+        "config": {"workload": w.name, "heads": w.h, "batch": w.batch, "cached_tokens": 4096,
+                   "kv_len": w.kv_max, "d_c": w.d_c, "d_rope": w.d_r, "d_qk_nope": w.d_n,
+                   "d_v": w.d_v, "cache": "contiguous bf16 [32, 4097, 576]",
+                   "layer_copies_rotated": COPIES},
+        "latent_cache_GBps": round(cache_gbps, 1),
+        "latent_cache_frac_of_hbm_peak": round(cache_gbps / HBM_PEAK_GBPS, 4),
+        "algorithmic_GBps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
+        "algorithmic_frac_of_hbm_peak": round(alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "tflops_frac_of_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "tokens_per_s": round(tok_s, 1),
+        "attention_kernel_ms": round(attn_avg, 5),
+        "roofline": {"bound": "hbm", "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "kernel": "decode_kernel<4,64> (split-K attention over the latent cache)",
+                     "algorithmic_bytes_per_launch": cache_bytes,
+                     "mfma_TFLOPs": round(flops * 0.9714 / (attn_avg * 1e-3) / 1e12, 1)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, t)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

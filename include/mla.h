@@ -1,0 +1,172 @@
+/*
+ * mla.h — C ABI of the MI355X (gfx950) absorbed Multi-head Latent Attention
+ * decode library (libmla.so).
+ *
+ * The method (pages: "MLA多头潜在注意力机制：低秩压缩与矩阵吸收实现高效推理"
+ * §2.2, §3.1, §3.2, §5.1, §5.2; the interview guide §6.2; the linear-algebra
+ * page, "潜在向量的压缩与上投影" and "解耦 RoPE"; the Gated-MLA page §2.6, §3.3):
+ *
+ *   Each cached token stores one row [ c_KV (d_c) ‖ RoPE(k_R, pos) (d_rope) ].
+ *   W_UK is absorbed into the query: q_abs = q_nope · W_UK_iᵀ (length d_c), so the
+ *   score of head i against token t is scale · (q_abs · c_t + RoPE(q_R) · k_R,t).
+ *   The softmax-weighted sum stays in latent space, o_lat = Σ_t p_t c_t, and W_UV
+ *   is applied once per head afterwards: out_i = o_lat · W_UV_i. With a gate,
+ *   out ⊙= sigmoid(x · W_G) channel-wise over the concatenated heads.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named as device pointers must be device memory of the current
+ *     HIP device; "host" pointers are ordinary host memory.
+ *   - All tensors are dense row-major in the order their shape is written.
+ *   - bf16 means IEEE bfloat16; every conversion to bf16 rounds to nearest even.
+ *   - Weight layouts follow the formula orientation: W_UK is [d_c][h*d_qk_nope]
+ *     and head i owns columns i*d_qk_nope .. (i+1)*d_qk_nope-1; W_UV likewise.
+ *   - RoPE rotates the pairs (x[2k], x[2k+1]) by pos * rope_base^(-2k/d_rope).
+ *   - Calls are asynchronous and ordered on `stream` (0 = the null stream). The
+ *     library never allocates, frees or synchronises, and keeps no state besides
+ *     a cached device-property query; it is safe to call from several threads.
+ *     Buffers passed in must stay alive until the stream has run the work.
+ *   - Errors: arguments are checked on the host before any launch, and a failed
+ *     check returns a status without touching the device. A launch failure
+ *     returns MLA_E_HIP. Device-side ranges that the host cannot see (kv_lens
+ *     contents, block-table entries) are bounds-checked in the kernels: an
+ *     out-of-range entry is skipped instead of being read or written, and the
+ *     result for that sequence is then undefined.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t mla_status;
+#define MLA_OK 0
+#define MLA_E_NULL 1        /* a required pointer is NULL */
+#define MLA_E_SHAPE 2       /* sizes inconsistent with each other */
+#define MLA_E_DTYPE 3       /* unknown dtype code */
+#define MLA_E_UNSUPPORTED 4 /* valid shape that this build has no kernel for */
+#define MLA_E_WORKSPACE 5   /* workspace too small */
+#define MLA_E_HIP 6         /* a HIP call or launch failed */
+
+#define MLA_F32 0  /* cache, weights and queries in fp32 (fp32 arithmetic throughout) */
+#define MLA_BF16 1 /* cache, weights and queries in bf16 (bf16 MFMA, fp32 accumulation) */
+
+/* Attention dimensions (per layer). */
+typedef struct {
+  int32_t n_heads;   /* h */
+  int32_t d_c;       /* latent width of the cached c_KV */
+  int32_t d_rope;    /* decoupled RoPE key width (0: no positional key) */
+  int32_t d_qk_nope; /* per-head query/key width without position */
+  int32_t d_v;       /* per-head value width */
+  float scale;       /* score scale; 0 selects 1/sqrt(d_qk_nope + d_rope) */
+  float rope_base;   /* 0 selects 10000 */
+  int32_t dtype;     /* MLA_F32 or MLA_BF16 */
+} mla_dims;
+
+/*
+ * Supported shapes. MLA_F32: any h <= 1024, d_c <= 1024, d_rope <= 256 and even,
+ * d_qk_nope <= 256, d_v <= 256 (a plain fp32 path for small layers).
+ * MLA_BF16: d_c = 512, d_rope in {0, 64}, d_qk_nope = 128, d_v = 128, with
+ * n_heads * n_q a multiple of 128 (any d_rope) or of 64 (d_rope = 0 only), and
+ * n_q dividing that row count into whole head groups (the DeepSeek-V2/V3
+ * attention shape and its position-free gated variant); with a gate, d_model a
+ * multiple of 16 and n_heads a multiple of 4. Paged caches need block_size a
+ * multiple of 32. Other shapes return MLA_E_UNSUPPORTED (or MLA_E_SHAPE).
+ */
+
+/*
+ * One-time weight absorption / packing (tutorial §3.2: "preprocess the absorbed
+ * weights once at load time"; the einsums `bhsd,hcd->bhsc` and `bhsc,hdc->bhsd`
+ * of §5.1).
+ *   w_uk   device [d_c][h*d_qk_nope], dims->dtype
+ *   w_uv   device [d_c][h*d_v],       dims->dtype
+ *   packed device buffer of *packed_bytes bytes, owned by the caller; its layout
+ *          is private to the library (per-head blocks in matrix-core fragment
+ *          order) and is what mla_decode / mla_decode_paged read.
+ * With packed == NULL the call only writes the needed size to *packed_bytes and
+ * returns MLA_OK (no device access). Otherwise *packed_bytes must hold at least
+ * that size (MLA_E_WORKSPACE if not).
+ */
+mla_status mla_absorb_weights(const mla_dims* dims, const void* w_uk, const void* w_uv,
+                              void* packed, size_t* packed_bytes, hipStream_t stream);
+
+/* Where the latent cache lives. Row width is d_c + d_rope elements of dims->dtype. */
+typedef struct {
+  const int32_t* block_table; /* device [batch][max_blocks] physical block ids; NULL = contiguous */
+  int32_t t_max;              /* contiguous: token slots per sequence, cache is [batch][t_max][row] */
+  int32_t block_size;         /* paged: tokens per block, pool is [n_blocks][block_size][row] */
+  int32_t max_blocks;         /* paged: entries per block-table row */
+  int32_t n_blocks;           /* paged: blocks in the pool (ids must lie in [0, n_blocks)) */
+} mla_cache_layout;
+
+/*
+ * Latent append (tutorial §5.2: append each new c_kv at its position instead of
+ * concatenating; interview guide §8.2; linear-algebra page "解耦 RoPE": the row
+ * is c_KV followed by the RoPE-rotated k_R).
+ *   cache  device buffer laid out as `layout` describes
+ *   c_kv   device [batch][n_new][d_c]    (already normalised by the caller)
+ *   k_r    device [batch][n_new][d_rope] unrotated; NULL iff d_rope == 0
+ *   pos0   device [batch]: slot of the first new token of each sequence; token j
+ *          goes to position pos0[b] + j and its k_R is rotated by that position
+ * The call writes only those n_new rows per sequence. Rows whose position falls
+ * outside the layout (or whose block id is out of range) are skipped. The caller
+ * owns the lengths and advances them once per step for all layers.
+ */
+mla_status mla_append_latent(const mla_dims* dims, void* cache, const mla_cache_layout* layout,
+                             int32_t batch, int32_t n_new, const void* c_kv, const void* k_r,
+                             const int32_t* pos0, hipStream_t stream);
+
+/* Per-call decode arguments. */
+typedef struct {
+  int32_t batch;               /* B */
+  int32_t n_q;                 /* new (query) tokens per sequence, >= 1 */
+  const int32_t* kv_lens;      /* device [B]: visible tokens per sequence, the n_q new ones
+                                  included (they must already be appended); query j of
+                                  sequence b is at position kv_lens[b] - n_q + j and
+                                  attends to positions 0 .. kv_lens[b] - n_q + j */
+  const int32_t* kv_lens_host; /* optional host copy of kv_lens: validated, and used to plan
+                                  the split of long sequences; NULL = plan from max_kv_len */
+  int32_t max_kv_len;          /* bound on every kv_lens[b] (required, >= n_q) */
+  const void* q_nope;          /* device [B][n_q][h][d_qk_nope], dims->dtype */
+  const void* q_rope;          /* device [B][n_q][h][d_rope] unrotated, NULL iff d_rope == 0 */
+  const void* packed_w;        /* device, from mla_absorb_weights */
+  const void* gate_x;          /* device [B][n_q][d_model] or NULL (no gate) */
+  const void* w_gate;          /* device [d_model][h*d_v] or NULL; both or neither */
+  int32_t d_model;             /* gate input width */
+  float* out;                  /* device [B][n_q][h*d_v] fp32, heads concatenated */
+  float* lse;                  /* device [B][n_q][h] fp32 log-sum-exp of the scores, or NULL */
+  void* workspace;             /* device scratch, or NULL to query its size */
+  size_t* workspace_bytes;     /* in: size of workspace; out (when workspace == NULL): needed */
+  int32_t num_splits;          /* 0: the planner chooses; > 0 forces token splits per sequence */
+  hipEvent_t ev_attn_begin;    /* optional events recorded on `stream` right before and */
+  hipEvent_t ev_attn_end;      /* after the split-K attention kernel (for timing); or NULL */
+} mla_decode_args;
+
+/*
+ * Absorbed decode over a contiguous cache [batch][t_max][d_c + d_rope] (tutorial
+ * §3.1 and §5.1; linear-algebra page "解耦 RoPE"; Gated-MLA page §2.6 for the
+ * gate). Writes args->out (and args->lse). Needs a workspace (query its size
+ * with workspace == NULL); MLA_E_WORKSPACE if *workspace_bytes is too small.
+ */
+mla_status mla_decode(const mla_dims* dims, const void* cache, int32_t t_max,
+                      const mla_decode_args* args, hipStream_t stream);
+
+/* The same over a paged pool [n_blocks][block_size][d_c + d_rope] addressed through
+ * block_table (device [batch][max_blocks]); block_size must be a multiple of 32. */
+mla_status mla_decode_paged(const mla_dims* dims, const void* pool, const int32_t* block_table,
+                            int32_t block_size, int32_t max_blocks, int32_t n_blocks,
+                            const mla_decode_args* args, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* mla_status_string(mla_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

@@ -1,0 +1,99 @@
+// Device-side helpers shared by the gfx950 kernels of libmla.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Generic -> LDS address-space pointer (the pointee must be __shared__ memory).
+__device__ __forceinline__ lds_char* lds_ptr(const void* p) { return (lds_char*)(p); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// bf16 bits -> fp32 (exact).
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return 0x7FC0;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// fp64 -> bf16 bits, round to nearest even, straight from the fp64 value (no
+// intermediate fp32 rounding): keep the top 8 significant bits of the 53.
+__device__ __forceinline__ uint16_t f64_to_bf16_bits(double x) {
+  uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+  const uint16_t sign = static_cast<uint16_t>((u >> 48) & 0x8000u);
+  const int e = static_cast<int>((u >> 52) & 0x7FF);
+  uint64_t m = u & 0x000FFFFFFFFFFFFFull;
+  if (e == 0x7FF) return m ? 0x7FC0 : static_cast<uint16_t>(sign | 0x7F80);
+  if (e == 0) return sign;  // fp64 subnormals are far below bf16's range
+  const int ue = e - 1023;  // unbiased exponent
+  m |= 1ull << 52;          // significand with the implicit bit, 53 bits
+  // bf16 keeps 8 significant bits for ue >= -126; below that the spacing is 2^-133.
+  int keep = 8;
+  if (ue < -126) keep = 8 - (-126 - ue);
+  if (keep <= 0) {
+    // rounds to 0 or to the smallest subnormal 2^-133
+    if (keep == 0 && m > (1ull << 52)) return static_cast<uint16_t>(sign | 1);
+    return sign;
+  }
+  const int drop = 53 - keep;
+  const uint64_t half = 1ull << (drop - 1);
+  const uint64_t rem = m & ((1ull << drop) - 1);
+  uint64_t q = m >> drop;
+  if (rem > half || (rem == half && (q & 1))) q += 1;
+  // q now has keep (or keep + 1 after a carry) significant bits
+  int ebits;
+  uint32_t mant;
+  if (ue >= -126) {
+    int ee = ue;
+    if (q >> 8) {  // carry out of 8 bits
+      q >>= 1;
+      ee += 1;
+    }
+    if (ee > 127) return static_cast<uint16_t>(sign | 0x7F80);
+    ebits = ee + 127;
+    mant = static_cast<uint32_t>(q & 0x7F);
+  } else {
+    // subnormal: value = q * 2^-133
+    if (q >> 7) {
+      ebits = 1;
+      mant = static_cast<uint32_t>(q & 0x7F);
+    } else {
+      ebits = 0;
+      mant = static_cast<uint32_t>(q);
+    }
+  }
+  return static_cast<uint16_t>(sign | (ebits << 7) | mant);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16_bits(lo)) | (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
+}
+
+}  // namespace mla

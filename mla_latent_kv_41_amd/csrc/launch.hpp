@@ -1,0 +1,89 @@
+// Host-side launchers for the kernels of libmla (one per translation unit).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Cache addressing shared by the kernels: contiguous when block_table == nullptr.
+struct CacheRef {
+  const void* data;
+  const int32_t* block_table;
+  int32_t t_max;       // contiguous: slots per sequence
+  int32_t block_size;  // paged
+  int32_t max_blocks;  // paged: table row length
+  int32_t n_blocks;    // paged: pool size
+};
+
+// ---------------------------------------------------------------- bf16 (MFMA) path
+hipError_t launch_pack_bf16(const uint16_t* w_uk, const uint16_t* w_uv, uint16_t* packed, int h,
+                            hipStream_t s);
+hipError_t launch_append(int dtype, void* cache, const CacheRef& c, int batch, int n_new, int d_c,
+                         int d_r, const void* c_kv, const void* k_r, const int32_t* pos0,
+                         double rope_base, hipStream_t s);
+
+struct QPrepArgs {
+  const uint16_t* q_nope;   // [M][h][128]
+  const uint16_t* q_rope;   // [M][h][64] or nullptr
+  const uint16_t* w_uk_pk;  // packed W_UK
+  const int32_t* kv_lens;
+  uint16_t* q_cat;          // [M][h][row]
+  int32_t M, n_q, h, d_r, max_kv_len;
+  float qscale;             // scale * log2(e)
+  double rope_base;
+};
+hipError_t launch_qprep_bf16(const QPrepArgs& a, hipStream_t s);
+
+struct DecodeArgs {
+  CacheRef cache;
+  const int32_t* kv_lens;
+  const uint16_t* q_cat;  // [M][h][row]
+  float* o_part;          // [B][S][n_q][h][512]
+  float* ml_part;         // [B][S][n_q][h][2]
+  int32_t batch, n_q, h, d_r, n_splits, chunk, max_kv_len;
+};
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
+
+struct CombineArgs {
+  const float* o_part;
+  const float* ml_part;
+  const int32_t* kv_lens;
+  const uint16_t* w_uv_pk;  // packed W_UV
+  const float* gate;        // [M][h*128] pre-activation gate logits or nullptr
+  float* out;               // [M][h*128]
+  float* lse;               // [M][h] or nullptr
+  int32_t batch, n_q, h, n_splits, chunk, max_kv_len;
+};
+hipError_t launch_combine_bf16(const CombineArgs& a, hipStream_t s);
+
+struct GateArgs {
+  const uint16_t* x;    // [M][d_model]
+  const uint16_t* w_g;  // [d_model][N]
+  float* g;             // [M][N] logits
+  int32_t M, d_model, N;
+};
+hipError_t launch_gate_bf16(const GateArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- fp32 path
+struct F32Args {
+  CacheRef cache;
+  const int32_t* kv_lens;
+  const float* q_nope;  // [M][h][d_n]
+  const float* q_rope;  // [M][h][d_r] or nullptr
+  const float* w_uk;    // [d_c][h*d_n]
+  const float* w_uv;    // [d_c][h*d_v]
+  const float* gate_x;  // [M][d_model] or nullptr
+  const float* w_gate;  // [d_model][h*d_v]
+  float* q_cat;         // ws [M][h][d_c + d_r]
+  float* scores;        // ws [M][h][max_kv_len]
+  float* o_lat;         // ws [M][h][d_c]
+  float* out;           // [M][h*d_v]
+  float* lse;           // [M][h] or nullptr
+  int32_t batch, n_q, h, d_c, d_r, d_n, d_v, d_model, max_kv_len;
+  float qscale;
+  double rope_base;
+};
+hipError_t launch_decode_f32(const F32Args& a, hipEvent_t ev0, hipEvent_t ev1, hipStream_t s);
+
+}  // namespace mla
