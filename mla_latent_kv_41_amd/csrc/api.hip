@@ -56,6 +56,8 @@ struct Plan {
   int hgroups;   // workgroups per (sequence, split)
   int n_splits;  // token ranges per sequence
   int chunk;     // tokens per range, a multiple of kTile
+  int comb_rows;    // combine: query rows per workgroup (power of two, <= 16)
+  int comb_splits;  // combine: partial rows staged per row and batch
 };
 
 Plan plan_bf16(const Resolved& r, const mla_decode_args* a) {
@@ -86,6 +88,11 @@ Plan plan_bf16(const Resolved& r, const mla_decode_args* a) {
   chunk = (chunk + kTile - 1) / kTile * kTile;
   p.chunk = static_cast<int>(chunk);
   p.n_splits = static_cast<int>((L + chunk - 1) / chunk);
+  // combine grid: (h, M / rows); halve the rows until the grid fills the CUs
+  const int M = a->batch * a->n_q;
+  p.comb_rows = 16;
+  while (p.comb_rows > 1 && static_cast<int64_t>(r.h) * ((M + p.comb_rows - 1) / p.comb_rows) < 256) p.comb_rows /= 2;
+  p.comb_splits = std::min(p.n_splits, 128 / p.comb_rows);
   return p;
 }
 
@@ -103,7 +110,7 @@ Workspace layout_ws(const Resolved& r, const mla_decode_args* a, const Plan* p) 
     off = align_up(off + M * r.h * row * 2);
     const size_t prow = static_cast<size_t>(a->batch) * p->n_splits * a->n_q * r.h;
     w.o_part = off;
-    off = align_up(off + prow * 512 * 4);
+    off = align_up(off + prow * 512 * 2);
     w.ml_part = off;
     off = align_up(off + prow * 2 * 4);
     if (a->gate_x) {
@@ -208,7 +215,7 @@ mla_status decode_impl(const mla_dims* dims, const CacheRef& cache, const mla_de
   q.d_r = r.d_r;
   q.max_kv_len = a->max_kv_len;
   q.qscale = qscale;
-  q.rope_base = r.rope_base;
+  for (int k = 0; k < r.d_r / 2 && k < 32; ++k) q.inv_freq[k] = pow(r.rope_base, -2.0 * k / r.d_r);
   if (launch_qprep_bf16(q, stream) != hipSuccess) return MLA_E_HIP;
 
   if (a->gate_x) {
@@ -226,7 +233,7 @@ mla_status decode_impl(const mla_dims* dims, const CacheRef& cache, const mla_de
   d.cache = cache;
   d.kv_lens = a->kv_lens;
   d.q_cat = q.q_cat;
-  d.o_part = reinterpret_cast<float*>(wsb + ws.o_part);
+  d.o_part = reinterpret_cast<uint16_t*>(wsb + ws.o_part);
   d.ml_part = reinterpret_cast<float*>(wsb + ws.ml_part);
   d.batch = a->batch;
   d.n_q = a->n_q;
@@ -253,6 +260,8 @@ mla_status decode_impl(const mla_dims* dims, const CacheRef& cache, const mla_de
   c.n_splits = p.n_splits;
   c.chunk = p.chunk;
   c.max_kv_len = a->max_kv_len;
+  c.rows_per_wg = p.comb_rows;
+  c.splits_per_batch = p.comb_splits;
   return launch_combine_bf16(c, stream) == hipSuccess ? MLA_OK : MLA_E_HIP;
 }
 

@@ -1,9 +1,9 @@
 // Split combine + W_UV up-projection (+ sigmoid output gate) for the bf16 path.
 //
-// Combine: the splits of one (query, head) row carry (O_s, m_s, l_s) with O_s and
-// l_s relative to their own running max m_s (base-2 units). The merge is the
-// max-subtracted softmax of the interview guide §7.3 applied across splits:
-//   M = max_s m_s,  L = Σ_s 2^(m_s - M) l_s,  o_lat = Σ_s 2^(m_s - M) O_s / L,
+// Combine: the splits of one (query, head) row carry (O_s / l_s, m_s, l_s), with
+// O_s and l_s relative to their own running max m_s (base-2 units). The merge is
+// the max-subtracted softmax of the interview guide §7.3 applied across splits:
+//   M = max_s m_s,  L = Σ_s 2^(m_s - M) l_s,  o_lat = Σ_s 2^(m_s - M) l_s (O_s/l_s) / L,
 //   lse = (M + log2 L) ln 2 (natural-log units).
 // Up-projection (MLA tutorial page §3.1 and the `bhsc,hdc->bhsd` einsum of §5.1):
 // out[m, i*128 + d] = o_lat[m, i, :] · W_UV_i[:, d], on v_mfma_f32_32x32x16_bf16.
@@ -15,83 +15,168 @@
 namespace mla {
 
 namespace {
-constexpr int kRows = 32;               // query rows per workgroup
-constexpr int kOStride = 512 * 2 + 16;  // bytes per o_lat row in LDS (padded)
 constexpr int kGateSplit = 16;          // K-splits of the gate GEMM
+constexpr int kAStride = 512 * 2 + 16;  // bytes per o_lat row in LDS (padded)
+constexpr int kPartSlots = 128;         // 1 KiB partial rows staged per batch
 }  // namespace
 
-// grid (h, ceil(M / 32)), 256 threads.
+// grid (h, ceil(M / rows_per_wg)), 256 threads. Workgroup (i, mb) produces
+// out[m][i*128 .. i*128+127] for rows m in [mb*RPW, mb*RPW + RPW).
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-  __shared__ __attribute__((aligned(16))) char s_o[kRows * kOStride];
+  __shared__ __attribute__((aligned(1024))) char s_part[kPartSlots * 1024];
+  __shared__ float s_stat[16][2];  // per row: max M and 1 / L
+  __shared__ int s_ns[16];         // per row: number of splits
+  __shared__ float s_w[kPartSlots];  // weight of each staged partial row
   const int i = blockIdx.x, mb = blockIdx.y;
-  const int w = threadIdx.x / 64, l = threadIdx.x % 64;
+  const int tid = threadIdx.x, l = tid % 64;
+  const int w = __builtin_amdgcn_readfirstlane(tid / 64);
   const int M = a.batch * a.n_q;
+  const int RPW = a.rows_per_wg, SB = a.splits_per_batch;
+  const int m0 = mb * RPW;
+  const int rows = min(RPW, M - m0);
 
-  // ---- phase 1: merge splits, one wave per row (rows w, w+4, ...)
-  for (int r = w; r < kRows; r += 4) {
-    const int m = kRows * mb + r;
-    uint32_t packed[4] = {0u, 0u, 0u, 0u};
-    if (m < M) {
-      const int b = m / a.n_q, j = m % a.n_q;
-      const int kv = min(a.kv_lens[b], a.max_kv_len);
-      const int ns = kv >= a.n_q ? min((kv + a.chunk - 1) / a.chunk, a.n_splits) : 0;
-      const int64_t row_stride = static_cast<int64_t>(a.n_q) * a.h;  // rows between splits
-      const int64_t row0 = (static_cast<int64_t>(b) * a.n_splits * a.n_q + j) * a.h + i;
-      float M_ = -INFINITY;
-      for (int s = 0; s < ns; ++s) M_ = fmaxf(M_, a.ml_part[(row0 + s * row_stride) * 2]);
-      const float mref = M_ == -INFINITY ? 0.f : M_;
-      float L = 0.f;
-      float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int s = 0; s < ns; ++s) {
-        const int64_t rr = row0 + s * row_stride;
-        const float ws = fast_exp2(a.ml_part[rr * 2] - mref);
-        L += ws * a.ml_part[rr * 2 + 1];
-        const f32x4* op = reinterpret_cast<const f32x4*>(a.o_part + rr * 512) + 2 * l;
-        const f32x4 v0 = op[0], v1 = op[1];
+  // W_UV_i fragments of this wave's 32 output columns, fetched up front
+  const u32x4* wv = reinterpret_cast<const u32x4*>(a.w_uv_pk) + ((static_cast<int64_t>(i) * 4 + w) * 32) * 64 + l;
+  u32x4 bfr[32];
+#pragma unroll
+  for (int ks = 0; ks < 32; ++ks) bfr[ks] = wv[ks * 64];
+
+  auto part_row = [&](int m, int sp) -> int64_t {  // row index of split sp of query row m, head i
+    const int b = m / a.n_q, j = m % a.n_q;
+    return ((static_cast<int64_t>(b) * a.n_splits + sp) * a.n_q + j) * a.h + i;
+  };
+
+  // ---- per row (one wave per row): split count, M = max_s m_s, L = Σ_s 2^(m_s - M) l_s
+  for (int r = w; r < rows; r += 4) {
+    const int m = m0 + r, b = m / a.n_q;
+    const int kv = min(a.kv_lens[b], a.max_kv_len);
+    const int ns = kv >= a.n_q ? min((kv + a.chunk - 1) / a.chunk, a.n_splits) : 0;
+    float mx = -INFINITY;
+    for (int sp = l; sp < ns; sp += 64) mx = fmaxf(mx, a.ml_part[part_row(m, sp) * 2]);
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    const float mref = mx == -INFINITY ? 0.f : mx;
+    float L = 0.f;
+    for (int sp = l; sp < ns; sp += 64) {
+      const int64_t pr = part_row(m, sp);
+      L += fast_exp2(a.ml_part[pr * 2] - mref) * a.ml_part[pr * 2 + 1];
+    }
+    for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
+    if (l == 0) {
+      s_stat[r][0] = mref;
+      s_stat[r][1] = L > 0.f ? 1.f / L : 0.f;
+      s_ns[r] = ns;
+      if (a.lse) a.lse[static_cast<int64_t>(m) * a.h + i] = L > 0.f ? (mx + __log2f(L)) * kLn2 : -INFINITY;
+    }
+  }
+  __syncthreads();
+  int ns_max = 0;
+  for (int r = 0; r < rows; ++r) ns_max = max(ns_max, s_ns[r]);
+
+  // ---- o_lat rows: Σ_s 2^(m_s - M) l_s / L · (O_s / l_s); lane owns 8 columns of
+  //      the rows r = w, w+4, ... (at most 4 per wave)
+  float o[4][8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[k][e] = 0.f;
+  for (int s0 = 0; s0 < ns_max; s0 += SB) {
+    // stage partial rows (r, s0 + q) into LDS slot r*SB + q (one 1 KiB wave load
+    // each) and their weights into s_w[slot] (one thread each); all loads issue
+    // before the single wait
+    for (int slot = w; slot < rows * SB; slot += 4) {
+      const int r = slot / SB, sp = s0 + slot % SB;
+      if (sp < s_ns[r])
+        __builtin_amdgcn_global_load_lds(a.o_part + part_row(m0 + r, sp) * 512 + l * 8,
+                                         (lds_void*)(lds_ptr(s_part) + slot * 1024), 16, 0, 0);
+    }
+    for (int slot = tid; slot < rows * SB; slot += 256) {
+      const int r = slot / SB, sp = s0 + slot % SB;
+      float wgt = 0.f;
+      if (sp < s_ns[r]) {
+        const int64_t pr = part_row(m0 + r, sp);
+        wgt = fast_exp2(a.ml_part[pr * 2] - s_stat[r][0]) * a.ml_part[pr * 2 + 1] * s_stat[r][1];
+      }
+      s_w[slot] = wgt;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int r = w + 4 * k;
+      if (r >= rows) break;
+      const int nq = min(SB, s_ns[r] - s0);
+      for (int q = 0; q < nq; ++q) {
+        const float wgt = s_w[r * SB + q];
+        const u32x4 v = *(lds_u32x4*)(lds_ptr(s_part) + (r * SB + q) * 1024 + l * 16);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          o[e] += ws * v0[e];
-          o[4 + e] += ws * v1[e];
+          o[k][2 * e] += wgt * __uint_as_float(v[e] << 16);
+          o[k][2 * e + 1] += wgt * __uint_as_float(v[e] & 0xFFFF0000u);
         }
       }
-      const float inv = L > 0.f ? 1.f / L : 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) packed[e] = pack_bf16x2(o[2 * e] * inv, o[2 * e + 1] * inv);
-      if (a.lse && l == 0) a.lse[static_cast<int64_t>(m) * a.h + i] = L > 0.f ? (M_ + __log2f(L)) * kLn2 : -INFINITY;
     }
-    u32x4 pv = {packed[0], packed[1], packed[2], packed[3]};
-    *reinterpret_cast<u32x4*>(s_o + r * kOStride + l * 16) = pv;
+    __syncthreads();
+  }
+
+  // ---- o_lat as a hi + lo pair of bf16 rows (hi = bf16(o), lo = bf16(o - hi)), so
+  //      the up-projection keeps about 16 significant bits of o_lat
+  char* s_hi = s_part;
+  char* s_lo = s_part + 32 * kAStride;
+  for (int r = w; r < 32; r += 4) {
+    u32x4 hv = {0u, 0u, 0u, 0u}, lv = {0u, 0u, 0u, 0u};
+    if (r < rows) {
+      const int k = r >> 2;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x0 = 0.f, x1 = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          if (kk == k) {
+            x0 = o[kk][2 * e];
+            x1 = o[kk][2 * e + 1];
+          }
+        const uint32_t h2 = pack_bf16x2(x0, x1);
+        hv[e] = h2;
+        lv[e] = pack_bf16x2(x0 - __uint_as_float(h2 << 16), x1 - __uint_as_float(h2 & 0xFFFF0000u));
+      }
+    }
+    *(lds_u32x4*)(lds_ptr(s_hi) + r * kAStride + l * 16) = hv;
+    *(lds_u32x4*)(lds_ptr(s_lo) + r * kAStride + l * 16) = lv;
   }
   __syncthreads();
 
-  // ---- phase 2: out[m][32w + ..] = o_lat[m][:] · W_UV_i[:, 32w + ..]
-  const u32x4* wv = reinterpret_cast<const u32x4*>(a.w_uv_pk) + ((static_cast<int64_t>(i) * 4 + w) * 32) * 64 + l;
-  const char* arow = s_o + (l & 31) * kOStride + (l >> 5) * 16;
+  // ---- out[m][i*128 + 32w + ..] = (o_hi + o_lo)[m][:] · W_UV_i[:, 32w + ..]
   f32x16 acc = {};
-#pragma unroll 8
+  const int arow = (l & 31) * kAStride + (l >> 5) * 16;
+#pragma unroll
   for (int ks = 0; ks < 32; ++ks) {
-    const u32x4 af = *reinterpret_cast<const u32x4*>(arow + ks * 32);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af), as_bf16x8(wv[ks * 64]), acc, 0, 0, 0);
+    const u32x4 ah = *(lds_u32x4*)(lds_ptr(s_hi) + arow + ks * 32);
+    const u32x4 al = *(lds_u32x4*)(lds_ptr(s_lo) + arow + ks * 32);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ah), as_bf16x8(bfr[ks]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(al), as_bf16x8(bfr[ks]), acc, 0, 0, 0);
   }
   const int width = a.h * 128;
   const int col = i * 128 + 32 * w + (l & 31);
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    const int m = kRows * mb + 8 * (v / 4) + 4 * (l >> 5) + (v & 3);
-    if (m >= M) continue;
-    float o = acc[v];
+    const int r = 8 * (v / 4) + 4 * (l >> 5) + (v & 3);
+    if (r >= rows) continue;
+    const int m = m0 + r;
+    float ov = acc[v];
     if (a.gate) {
       float g = 0.f;
       for (int ks = 0; ks < kGateSplit; ++ks) g += a.gate[(static_cast<int64_t>(ks) * M + m) * width + col];
-      o *= 1.f / (1.f + __expf(-g));
+      ov *= 1.f / (1.f + __expf(-g));
     }
-    a.out[static_cast<int64_t>(m) * width + col] = o;
+    a.out[static_cast<int64_t>(m) * width + col] = ov;
   }
 }
 
 hipError_t launch_combine_bf16(const CombineArgs& a, hipStream_t s) {
   const int M = a.batch * a.n_q;
-  combine_kernel<<<dim3(a.h, (M + kRows - 1) / kRows), 256, 0, s>>>(a);
+  if (a.rows_per_wg < 1 || a.rows_per_wg > 16 || a.rows_per_wg * a.splits_per_batch > kPartSlots)
+    return hipErrorInvalidValue;
+  combine_kernel<<<dim3(a.h, (M + a.rows_per_wg - 1) / a.rows_per_wg), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -31,7 +31,7 @@ struct QPrepArgs {
   uint16_t* q_cat;          // [M][h][row]
   int32_t M, n_q, h, d_r, max_kv_len;
   float qscale;             // scale * log2(e)
-  double rope_base;
+  double inv_freq[32];      // rope_base^(-2k/d_r), computed on the host in fp64
 };
 hipError_t launch_qprep_bf16(const QPrepArgs& a, hipStream_t s);
 
@@ -39,21 +39,23 @@ struct DecodeArgs {
   CacheRef cache;
   const int32_t* kv_lens;
   const uint16_t* q_cat;  // [M][h][row]
-  float* o_part;          // [B][S][n_q][h][512]
+  uint16_t* o_part;       // [B][S][n_q][h][512] bf16, normalised O / l
   float* ml_part;         // [B][S][n_q][h][2]
   int32_t batch, n_q, h, d_r, n_splits, chunk, max_kv_len;
 };
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
 
 struct CombineArgs {
-  const float* o_part;
-  const float* ml_part;
+  const uint16_t* o_part;  // [B][S][n_q][h][512] bf16
+  const float* ml_part;    // [B][S][n_q][h][2] (m, l)
   const int32_t* kv_lens;
   const uint16_t* w_uv_pk;  // packed W_UV
   const float* gate;        // [M][h*128] pre-activation gate logits or nullptr
   float* out;               // [M][h*128]
   float* lse;               // [M][h] or nullptr
   int32_t batch, n_q, h, n_splits, chunk, max_kv_len;
+  int32_t rows_per_wg;       // query rows per workgroup, 1..16
+  int32_t splits_per_batch;  // partial rows staged per row and batch (rows * splits <= 128)
 };
 hipError_t launch_combine_bf16(const CombineArgs& a, hipStream_t s);
 

@@ -55,10 +55,14 @@ hipError_t launch_pack_bf16(const uint16_t* w_uk, const uint16_t* w_uv, uint16_t
 }
 
 // grid (h, 4): head i, quarter cq of the 512 latent columns; 4 waves, wave w owns
-// the 32 columns of block nb = 4cq + w and loops over 32-row blocks of M.
+// the 32 columns of block nb = 4cq + w and loops over 32-row blocks of M. The
+// 32 x 128 bf16 result block is staged in LDS so Q_cat is written in 256-byte rows.
 __global__ __launch_bounds__(256) void qprep_kernel(QPrepArgs a) {
+  constexpr int kStride = 128 * 2 + 16;  // bytes per staged row (padded)
+  __shared__ __attribute__((aligned(16))) char s_q[32 * kStride];
   const int i = blockIdx.x, cq = blockIdx.y;
-  const int w = threadIdx.x / 64, l = threadIdx.x % 64;
+  const int tid = threadIdx.x, l = tid % 64;
+  const int w = __builtin_amdgcn_readfirstlane(tid / 64);
   const int nb = 4 * cq + w;
   const int row = 512 + a.d_r;
   const u32x4* wk = reinterpret_cast<const u32x4*>(a.w_uk_pk) + ((static_cast<int64_t>(i) * 16 + nb) * 8) * 64 + l;
@@ -69,35 +73,50 @@ __global__ __launch_bounds__(256) void qprep_kernel(QPrepArgs a) {
     const int m_a = 32 * mb + l % 32;
     f32x16 acc = {};
     const u32x4* qn = reinterpret_cast<const u32x4*>(a.q_nope + (static_cast<int64_t>(m_a) * a.h + i) * 128) + (l / 32);
+    u32x4 af[8];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      u32x4 af = {0u, 0u, 0u, 0u};
-      if (m_a < a.M) af = qn[2 * ks];
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af), as_bf16x8(bfr[ks]), acc, 0, 0, 0);
-    }
-    const int c = 32 * nb + l % 32;
+    for (int ks = 0; ks < 8; ++ks) af[ks] = m_a < a.M ? qn[2 * ks] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[ks]), as_bf16x8(bfr[ks]), acc, 0, 0, 0);
+    // stage: row 8(v/4) + 4(l/32) + v%4, column 32w + l%32 of the block
+    __syncthreads();
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int m = 32 * mb + 8 * (v / 4) + 4 * (l / 32) + v % 4;
-      if (m < a.M) a.q_cat[(static_cast<int64_t>(m) * a.h + i) * row + c] = f32_to_bf16_bits(acc[v] * a.qscale);
+      const int r = 8 * (v / 4) + 4 * (l / 32) + v % 4;
+      *(__attribute__((address_space(3))) uint16_t*)(lds_ptr(s_q) + r * kStride + (32 * w + (l & 31)) * 2) =
+          f32_to_bf16_bits(acc[v] * a.qscale);
+    }
+    __syncthreads();
+    // 32 rows x 16 chunks of 16 B: two chunks per thread
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int q = tid + 256 * k, r = q / 16, ch = q % 16;
+      const int m = 32 * mb + r;
+      if (m < a.M) {
+        const u32x4 v = *(lds_u32x4*)(lds_ptr(s_q) + r * kStride + ch * 16);
+        *reinterpret_cast<u32x4*>(a.q_cat + (static_cast<int64_t>(m) * a.h + i) * row + 128 * cq + ch * 8) = v;
+      }
     }
   }
   if (a.d_r == 0) return;
-  // RoPE of q_R for rows m = cq (mod 4): angle pos * base^(-2k/d_r) in fp64.
+  // RoPE of q_R for rows m = cq (mod 4): angle pos * inv_freq[k], formed and reduced
+  // modulo 2π in fp64; sine and cosine of the reduced angle in fp32.
   const int half = a.d_r / 2;
   const int rows = (a.M - cq + 3) / 4;
-  for (int idx = threadIdx.x; idx < rows * half; idx += blockDim.x) {
+  for (int idx = tid; idx < rows * half; idx += blockDim.x) {
     const int m = 4 * (idx / half) + cq, k = idx % half;
     const int b = m / a.n_q, j = m % a.n_q;
     const int kv = min(a.kv_lens[b], a.max_kv_len);
-    const int64_t pos = static_cast<int64_t>(kv) - a.n_q + j;
-    double sn, cs;
-    sincos(static_cast<double>(pos) * pow(a.rope_base, -2.0 * k / a.d_r), &sn, &cs);
+    const double theta = static_cast<double>(kv - a.n_q + j) * a.inv_freq[k];
+    const double red = theta - 6.283185307179586 * rint(theta * 0.15915494309189535);
+    float sn, cs;
+    sincosf(static_cast<float>(red), &sn, &cs);
     const uint16_t* qr = a.q_rope + (static_cast<int64_t>(m) * a.h + i) * a.d_r;
-    const double x0 = bf16_bits_to_f32(qr[2 * k]), x1 = bf16_bits_to_f32(qr[2 * k + 1]);
+    const float x0 = bf16_bits_to_f32(qr[2 * k]), x1 = bf16_bits_to_f32(qr[2 * k + 1]);
     uint16_t* dst = a.q_cat + (static_cast<int64_t>(m) * a.h + i) * row + 512;
-    dst[2 * k] = f32_to_bf16_bits(static_cast<float>((x0 * cs - x1 * sn) * a.qscale));
-    dst[2 * k + 1] = f32_to_bf16_bits(static_cast<float>((x0 * sn + x1 * cs) * a.qscale));
+    dst[2 * k] = f32_to_bf16_bits((x0 * cs - x1 * sn) * a.qscale);
+    dst[2 * k + 1] = f32_to_bf16_bits((x0 * sn + x1 * cs) * a.qscale);
   }
 }
 

@@ -57,9 +57,9 @@ def call_decode(d, *, batch=32, n_q=1, max_kv_len=4097, t_max=4097, host=None, n
 def test_workspace_query_deepseek_shape():
     st, n = call_decode(ds_dims())
     assert st == mla.MLA_OK
-    # q_cat + 8 splits of fp32 partial outputs and (m, l) per (sequence, head)
+    # q_cat + 8 splits of bf16 partial rows and fp32 (m, l) per (sequence, head)
     q_cat = 32 * 128 * 576 * 2
-    parts = 32 * 8 * 128 * (512 + 2) * 4
+    parts = 32 * 8 * 128 * (512 * 2 + 2 * 4)
     assert q_cat + parts <= n <= q_cat + parts + 3 * 256
 
 
@@ -118,5 +118,5 @@ def test_split_plan_sizes():
             chunk = -(-(-(-L // s)) // 32) * 32
             splits = -(-L // chunk)
             q_cat = 4 * 128 * 576 * 2
-            parts = 4 * splits * 128 * 514 * 4
+            parts = 4 * splits * 128 * (512 * 2 + 2 * 4)
             assert q_cat + parts <= n <= q_cat + parts + 3 * 256
