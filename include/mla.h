@@ -143,8 +143,10 @@ typedef struct {
   void* workspace;             /* device scratch, or NULL to query its size */
   size_t* workspace_bytes;     /* in: size of workspace; out (when workspace == NULL): needed */
   int32_t num_splits;          /* 0: the planner chooses; > 0 forces token splits per sequence */
-  hipEvent_t ev_attn_begin;    /* optional events recorded on `stream` right before and */
-  hipEvent_t ev_attn_end;      /* after the split-K attention kernel (for timing); or NULL */
+  hipEvent_t ev_attn_begin;    /* optional timing events (both or neither, else MLA_E_NULL): */
+  hipEvent_t ev_attn_end;      /* bf16 path: stamped by the split-K attention dispatch itself
+                                  (start and end of that kernel); fp32 path: recorded on
+                                  `stream` before and after its attention kernels */
 } mla_decode_args;
 
 /*

@@ -7,7 +7,7 @@
 
 #include <algorithm>
 
-#include "../../include/mla.h"
+#include "mla.h"
 #include "launch.hpp"
 
 using namespace mla;
@@ -134,6 +134,7 @@ mla_status check_decode(const Resolved& r, const mla_decode_args* a) {
   if (a->batch <= 0 || a->n_q <= 0 || a->max_kv_len < a->n_q) return MLA_E_SHAPE;
   if (!a->workspace_bytes) return MLA_E_NULL;
   if ((a->gate_x == nullptr) != (a->w_gate == nullptr)) return MLA_E_NULL;
+  if ((a->ev_attn_begin == nullptr) != (a->ev_attn_end == nullptr)) return MLA_E_NULL;
   if (a->gate_x && a->d_model <= 0) return MLA_E_SHAPE;
   if (a->num_splits < 0) return MLA_E_SHAPE;
   if (a->kv_lens_host) {
@@ -242,9 +243,7 @@ mla_status decode_impl(const mla_dims* dims, const CacheRef& cache, const mla_de
   d.n_splits = p.n_splits;
   d.chunk = p.chunk;
   d.max_kv_len = a->max_kv_len;
-  if (a->ev_attn_begin && hipEventRecord(a->ev_attn_begin, stream) != hipSuccess) return MLA_E_HIP;
-  if (launch_decode_bf16(d, stream) != hipSuccess) return MLA_E_HIP;
-  if (a->ev_attn_end && hipEventRecord(a->ev_attn_end, stream) != hipSuccess) return MLA_E_HIP;
+  if (launch_decode_bf16(d, stream, a->ev_attn_begin, a->ev_attn_end) != hipSuccess) return MLA_E_HIP;
 
   CombineArgs c{};
   c.o_part = d.o_part;

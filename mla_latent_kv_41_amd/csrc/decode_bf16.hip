@@ -15,12 +15,16 @@
 // 128 heads sharing one latent make them dense: each bf16 cache element loaded
 // from HBM feeds 2*R multiply-adds.
 //
-// Each wave (one per SIMD) owns 32 query rows end to end: their Q_cat fragments
-// stay in VGPRs, their Oᵀ accumulators (512 columns x 32 rows fp32 = 256 registers
-// per lane) in AGPRs, and their softmax state in lanes. The value MFMA takes the
-// tile's 32 tokens in the order the score MFMA leaves them in its accumulator, so
-// P goes from the score accumulator to the value MFMA without leaving registers.
-// Waves share only the tile buffers.
+// Work split inside a workgroup (one wave per SIMD): for the scores and the
+// softmax, wave w owns query rows 32w .. 32w+31 (their Q_cat fragments stay in
+// VGPRs, their softmax state in lanes). For the value contraction it owns latent
+// columns 32*CBW*w .. +32*CBW of every row (Oᵀ accumulators, 16 blocks of 32x32
+// fp32 = 256 registers per lane, in AGPRs), so each cache element is transposed
+// out of LDS once per workgroup rather than once per wave. P travels between the
+// two through an 8 KiB LDS buffer, written in the B-operand order of the value
+// MFMA: the value MFMA takes the tile's 32 tokens in the order the score MFMA
+// leaves them in its accumulator. Two barriers per tile: one for the tile (and
+// the release of the previous tile and of P), one for P.
 //
 // Pipelining: 128-row workgroups (one per CU) keep four tile buffers, so the
 // direct-to-LDS loads of a tile are issued three tiles before it is consumed;
@@ -47,6 +51,7 @@
 // coalesced through LDS) and (m, l) in fp32; the combine kernel merges splits.
 #include "common.hpp"
 #include "launch.hpp"
+#include <hip/hip_ext.h>
 
 namespace mla {
 
@@ -71,12 +76,35 @@ struct Cfg {
   static constexpr int R = 32 * NW;                        // query rows per workgroup
   static constexpr int TILE_BYTES = kTileT * ROWB;
   static constexpr int LOADS = (kTileT * CH) / (64 * NW);  // 16-B loads per lane per tile
+  static constexpr int CBW = 16 / NW;                      // value column blocks per wave
+  static constexpr int RB = NW;                            // row blocks of 32 query rows
+  static_assert((kTileT * CH) % (64 * NW) == 0, "tile loads per wave");
+  static_assert(32 * CBW * R * 2 <= TILE_BYTES, "epilogue staging fits a tile buffer");
 };
 
 template <int V>
 struct Ic {
   static constexpr int value = V;
 };
+
+// One 16-byte-per-lane direct-to-LDS load: lane l's 16 bytes at buffer offset
+// voff + soff land at LDS address lds + 16*l. Issued from asm so that the
+// compiler's wait insertion does not track it (it would otherwise wait for all
+// such loads before unrelated LDS reads); the kernel bounds these loads with
+// explicit vmcnt waits. M0 (the LDS base) is restored, and no register is written.
+__device__ __forceinline__ void dma_b128(const u32x4& rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile("" : "+s"(soff), "+s"(lds));  // registers, never folded literals
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory");
+}
 
 // s_waitcnt that bounds only the vector-memory counter (lgkm and exp left free).
 template <int N>
@@ -90,14 +118,16 @@ __device__ __forceinline__ void wait_vm() {
 template <int NW, int DR>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   using C = Cfg<NW, DR>;
-  constexpr int NBUF = C::NBUF;
+  constexpr int NBUF = C::NBUF, CBW = C::CBW, RB = C::RB;
   // Tile buffers as distinct arrays: reads of one are provably independent of the
   // direct-to-LDS loads landing in another, so they need no load wait.
   __shared__ __attribute__((aligned(1024))) char s_tile0[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char s_tile1[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char s_tile2[NBUF > 2 ? C::TILE_BYTES : 16];
   __shared__ __attribute__((aligned(1024))) char s_tile3[NBUF > 3 ? C::TILE_BYTES : 16];
-  __shared__ int s_restart[3];  // restart requests of tile i live in slot i % 3
+  __shared__ __attribute__((aligned(16))) char s_p[RB * 2 * 1024];  // P fragments [row block][k-step][lane]
+  __shared__ float s_inv[C::R];                                      // 1 / l per row (epilogue)
+  __shared__ int s_restart;
 
   const int tid = threadIdx.x, l = tid % 64;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64);  // wave index, uniform
@@ -119,20 +149,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const int n_tiles = (t_end - t_begin + kTileT - 1) / kTileT;
 
   const int HG = C::R / a.n_q;  // heads per workgroup
-  // this lane's row r = 32w + l%32 (lanes l and l^32 hold the same row)
+  // this lane's score row r = 32w + l%32 (lanes l and l^32 hold the same row)
   const int r_own = 32 * w + (l & 31);
   const int j_own = r_own / HG;
   const int head_own = hg * HG + r_own % HG;
   const int vis_own = kv - a.n_q + j_own;  // last visible position of this row
-
-  // ---- Q_cat fragments (B operand of the score MFMA): k = 16ks + 8(l/32) + e
-  u32x4 qf[C::KS];
-  {
-    const int64_t m = static_cast<int64_t>(b) * a.n_q + j_own;
-    const u32x4* qp = reinterpret_cast<const u32x4*>(a.q_cat + (m * a.h + head_own) * C::ROW) + (l >> 5);
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) qf[ks] = qp[2 * ks];
-  }
 
   // ---- tile loads: wave load n' = n*NW + w fills LDS [n'*1024, +1024) = column
   //      group G = n'/4, rows 8(n'%4) + l/8, chunk position l%8. Its source is
@@ -147,10 +168,22 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 
   const char* cache = static_cast<const char*>(a.cache.data);
   const bool paged = a.cache.block_table != nullptr;
+  // physical block of tile `it` (paged cache); out-of-range entries read block 0.
+  // The table is read-only here: reading it through the constant address space
+  // makes the uniform lookup a scalar load, which does not wait on tile loads.
+  const __attribute__((address_space(4))) int32_t* table =
+      (const __attribute__((address_space(4))) int32_t*)(a.cache.block_table);
+  auto page_id = [&](int it) __attribute__((always_inline)) -> int {
+    const int blk = (t_begin + it * kTileT) / a.cache.block_size;
+    const int id = table[static_cast<int64_t>(b) * a.cache.max_blocks + blk];
+    return (id < 0 || id >= a.cache.n_blocks) ? 0 : id;
+  };
+  int pg_next = paged ? page_id(0) : 0;  // block of the next tile to issue, read one issue ahead
 
   // A 32-token tile never straddles a block (ranges start at multiples of 32 and
   // blocks are multiples of 32 tokens), so one buffer resource covers the tile;
-  // its size bound keeps every load of the tile inside it.
+  // its size bound keeps every load of the tile inside it. Tiles are issued in
+  // order, so the block of tile it + 1 is fetched while tile it is issued.
   auto issue_tile = [&](int it, char* tile) __attribute__((always_inline)) {
     const int t0 = t_begin + it * kTileT;
     lds_char* dst = lds_ptr(tile);
@@ -158,13 +191,13 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     if (!paged) {
       base = cache + (static_cast<int64_t>(b) * a.cache.t_max + t0) * C::ROWB;
     } else {
-      const int blk = t0 / a.cache.block_size;
-      int id = a.cache.block_table[static_cast<int64_t>(b) * a.cache.max_blocks + blk];
-      if (id < 0 || id >= a.cache.n_blocks) id = 0;  // out-of-range entry: stay in bounds
-      base = cache + (static_cast<int64_t>(id) * a.cache.block_size + t0 % a.cache.block_size) * C::ROWB;
+      base = cache + (static_cast<int64_t>(pg_next) * a.cache.block_size + t0 % a.cache.block_size) * C::ROWB;
+      if (it + 1 < n_tiles) pg_next = page_id(it + 1);
     }
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, C::TILE_BYTES, 0x00020000);
+    // raw buffer resource: base, stride 0, size bound TILE_BYTES
+    const uint64_t ba = reinterpret_cast<uint64_t>(base);
+    const u32x4 rsrc = {static_cast<uint32_t>(ba), static_cast<uint32_t>(ba >> 32) & 0xFFFFu,
+                        static_cast<uint32_t>(C::TILE_BYTES), 0x00020000u};
     const bool full = t0 + kTileT <= t_end;
     const int last = t_end - 1 - t0;  // rows past it re-read row `last` (masked later)
 #pragma unroll
@@ -181,7 +214,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         voff = static_cast<uint32_t>(min(row, last) * C::ROWB) + c16;
         soff = static_cast<uint32_t>(G * 128);
       }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + np * 1024), 16, voff, soff, 0, 0);
+      dma_b128(rsrc, voff, soff, static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst + np * 1024)));
     }
   };
 
@@ -214,11 +247,15 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     }
   }
 
-  f32x16 acc[16];  // Oᵀ: column block cb (32 latent columns) x this wave's 32 rows
+  u32x4 qf[C::KS];  // this row's Q_cat fragments (loaded below)
+
+  // Oᵀ accumulators: column block CBW*w + cbl (32 latent columns) x row block rb
+  // (32 query rows), acc[cbl * RB + rb]
+  f32x16 acc[CBW * RB];
   float m_ref = -INFINITY;   // this row's fixed reference max
   float m_seen = -INFINITY;  // largest score this row has seen
   float l_run = 0.f;
-  if (tid < 3) s_restart[tid] = 0;
+  if (tid == 0) s_restart = 0;
 
   // ---- scores: Sᵀ[32 tokens][32 rows of this wave], four fragments in flight
   auto scores = [&](const char* tile) __attribute__((always_inline)) {
@@ -241,7 +278,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     u32x4 p[2];
     bool overrun;
   };
-  auto softmax = [&](f32x16 sc, int it) __attribute__((always_inline)) {
+  auto softmax = [&](f32x16 sc, int it, bool allow_restart) __attribute__((always_inline)) {
     const int t0 = t_begin + it * kTileT;
     const int lim = min(t_end - 1, vis_own);  // last token this row may see
     if (t0 + kTileT - 1 > min(t_end - 1, kv - a.n_q)) {
@@ -251,49 +288,57 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         if (tok > lim) sc[v] = -INFINITY;
       }
     }
-    float mx = sc[0];
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
 #pragma unroll
-    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sc[v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    for (int v = 3; v < 15; v += 2) mx = fmaxf(fmaxf(mx, sc[v]), sc[v + 1]);
+    mx = half_max(fmaxf(mx, sc[15]));
     m_seen = fmaxf(m_seen, mx);
     // first visible tile of the row: nothing accumulated yet, so set the reference
     if (m_ref == -INFINITY) m_ref = mx;
     Soft r;
-    r.overrun = mx > m_ref + kHeadroom;
+    r.overrun = allow_restart && mx > m_ref + kHeadroom;
     const float mref = m_ref == -INFINITY ? 0.f : m_ref;
-    float psum = 0.f;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int v = 0; v < 16; v += 2) {
       const float p0 = fast_exp2(sc[v] - mref), p1 = fast_exp2(sc[v + 1] - mref);
-      psum += p0 + p1;
+      ps[(v >> 1) & 3] += p0 + p1;
       r.p[v >> 3][(v >> 1) & 3] = pack_bf16x2(p0, p1);
     }
-    psum += __shfl_xor(psum, 32);
-    l_run += psum;
+    l_run += half_sum((ps[0] + ps[1]) + (ps[2] + ps[3]));
     return r;
   };
 
-  // ---- values: Oᵀ[c][r] += Σ_t Cᵀ[c][t] · Pᵀ[t][r] for all 512 columns; the 32
-  //      (k-step, column block) fragments stream through a four-deep window of
-  //      transposed reads so each MFMA finds its operand already loaded
-  auto pv = [&](const char* tile, const Soft& sp) __attribute__((always_inline)) {
+  // ---- values for this wave's CBW column blocks and every row block:
+  //      Oᵀ[c][r] += Σ_t Cᵀ[c][t] · Pᵀ[t][r]; P of all rows comes from LDS, the
+  //      2*CBW transposed cache fragments stream through a four-deep window
+  auto pv = [&](const char* tile) __attribute__((always_inline)) {
     auto load = [&](int f) __attribute__((always_inline)) {
-      const int kk = f >> 4, cb = f & 15;
+      const int kk = f / CBW, cb = CBW * w + f % CBW;
       lds_char* tb = lds_ptr(tile) + kk * 16 * 128 + (cb >> 1) * 4096;
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tb + va_off[0][cb & 1]));
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tb + va_off[1][cb & 1]));
       const i16x8 af = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       return af;
     };
-    i16x8 frag[4];
+    u32x4 pb[2][RB];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) frag[f] = load(f);
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-    for (int f = 0; f < 32; ++f) {
-      const int kk = f >> 4, cb = f & 15;
-      acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, frag[f & 3]),
-                                                       as_bf16x8(sp.p[kk]), acc[cb], 0, 0, 0);
-      if (f + 4 < 32) frag[f & 3] = load(f + 4);
+      for (int rb = 0; rb < RB; ++rb) pb[kk][rb] = *(lds_u32x4*)(lds_ptr(s_p) + (rb * 2 + kk) * 1024 + l * 16);
+    constexpr int NF = 2 * CBW;
+    constexpr int WIN = NF < 4 ? NF : 4;
+    i16x8 frag[WIN];
+#pragma unroll
+    for (int f = 0; f < WIN; ++f) frag[f] = load(f);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int kk = f / CBW, cbl = f % CBW;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        acc[cbl * RB + rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, frag[f % WIN]), as_bf16x8(pb[kk][rb]), acc[cbl * RB + rb], 0, 0, 0);
+      if (f + WIN < NF) frag[f % WIN] = load(f + WIN);
     }
   };
 
@@ -306,8 +351,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   };
 
   // step i: tile i in buffer i % NBUF; tiles up to i + NBUF - 2 were issued before.
-  // Returns true when a restart was requested at tile i - 1.
-  auto step = [&](auto kc, int i) __attribute__((always_inline)) -> bool {
+  // Returns true when some row asked for a restart at tile i.
+  auto step = [&](auto kc, int i, bool allow_restart) __attribute__((always_inline)) -> bool {
     constexpr int K = decltype(kc)::value;
     const int ahead = min(n_tiles - 1, i + NBUF - 2) - i;  // tiles issued after tile i
     if constexpr (NBUF == 4) {
@@ -317,70 +362,95 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     } else {
       wait_vm<0>();
     }
-    __syncthreads();  // tile i everywhere; every wave is done with tile i-1
-    if (i > 0 && s_restart[(i + 2) % 3]) return true;  // request made at tile i-1
-    if (tid == 0) s_restart[(i + 1) % 3] = 0;         // slot of tile i-2, read at tile i-1
+    lds_barrier();  // tile i everywhere; every wave is done with tile i-1 and with P
     if (i + NBUF - 1 < n_tiles) issue_tile(i + NBUF - 1, tile_ptr(Ic<(K + NBUF - 1) % NBUF>{}));
-    const Soft cur = softmax(scores(tile_ptr(kc)), i);
-    if (__builtin_amdgcn_ballot_w64(cur.overrun)) s_restart[i % 3] = 1;
-    pv(tile_ptr(kc), cur);
-    return false;
+    const Soft cur = softmax(scores(tile_ptr(kc)), i, allow_restart);
+    *(lds_u32x4*)(lds_ptr(s_p) + (w * 2 + 0) * 1024 + l * 16) = cur.p[0];
+    *(lds_u32x4*)(lds_ptr(s_p) + (w * 2 + 1) * 1024 + l * 16) = cur.p[1];
+    if (__builtin_amdgcn_ballot_w64(cur.overrun) && l == 0) s_restart = 1;
+    lds_barrier();  // P of every row
+    const int restart = s_restart;
+    pv(tile_ptr(kc));
+    return restart != 0;
   };
 
-  for (int restarts = 0;; ++restarts) {
-#pragma unroll
-    for (int cb = 0; cb < 16; ++cb) acc[cb] = f32x16{};
-    l_run = 0.f;
+  auto prologue = [&]() __attribute__((always_inline)) {
+    if (paged) pg_next = page_id(0);
 #pragma unroll
     for (int k = 0; k < NBUF - 1; ++k)
       if (k < n_tiles) issue_tile(k, k == 0 ? s_tile0 : k == 1 ? s_tile1 : s_tile2);
+  };
+  prologue();
+
+  // ---- Q_cat fragments (B operand of the score MFMA): k = 16ks + 8(l/32) + e,
+  //      loaded while the first tiles are in flight; the wait covers both, so no
+  //      later wait for these loads lands inside the tile loop
+  {
+    const int64_t m = static_cast<int64_t>(b) * a.n_q + j_own;
+    const u32x4* qp = reinterpret_cast<const u32x4*>(a.q_cat + (m * a.h + head_own) * C::ROW) + (l >> 5);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) qf[ks] = qp[2 * ks];
+  }
+  wait_vm<0>();
+
+  for (int pass = 0;; ++pass) {
+    const bool allow_restart = pass < kMaxRestarts;  // the last pass keeps every score
+#pragma unroll
+    for (int k = 0; k < CBW * RB; ++k) acc[k] = f32x16{};
+    l_run = 0.f;
+    if (pass > 0) prologue();
     bool restart = false;
     for (int i = 0; i < n_tiles && !restart; i += NBUF) {
-      restart = step(Ic<0>{}, i);
-      if (!restart && i + 1 < n_tiles) restart = step(Ic<1>{}, i + 1);
+      restart = step(Ic<0>{}, i, allow_restart);
+      if (!restart && i + 1 < n_tiles) restart = step(Ic<1>{}, i + 1, allow_restart);
       if constexpr (NBUF == 4) {
-        if (!restart && i + 2 < n_tiles) restart = step(Ic<2>{}, i + 2);
-        if (!restart && i + 3 < n_tiles) restart = step(Ic<3>{}, i + 3);
+        if (!restart && i + 2 < n_tiles) restart = step(Ic<2>{}, i + 2, allow_restart);
+        if (!restart && i + 3 < n_tiles) restart = step(Ic<3>{}, i + 3, allow_restart);
       }
     }
-    wait_vm<0>();
-    __syncthreads();
-    if (!restart) restart = s_restart[(n_tiles - 1) % 3] != 0;  // request at the last tile
-    if (!restart || restarts == kMaxRestarts) break;
-    // restart the range with the largest score seen as every row's reference
-    __syncthreads();
-    if (tid < 3) s_restart[tid] = 0;
+    wait_vm<0>();  // this wave's loads have landed (a restart leaves some in flight)
+    if (!restart) break;
+    // restart the range with the largest score seen as every row's reference; the
+    // barrier orders every wave's drained loads and flag read before the reset
+    lds_barrier();
+    if (tid == 0) s_restart = 0;
     m_ref = m_seen;
-    __syncthreads();
   }
 
-  // ---- epilogue: normalised partial O/l as bf16 rows, staged in LDS (wave w uses
-  //      tile buffer w) so every global store is a whole 1 KiB row; every wave is
-  //      past the last tile (barrier above)
-  const int64_t part_row0 = (static_cast<int64_t>(b) * a.n_splits + s) * a.n_q;
-  char* stg = w == 0 ? s_tile0 : w == 1 ? s_tile1 : w == 2 ? s_tile2 : s_tile3;  // [32][64 chunks], chunk ^ (row & 15)
-  {
-    const int rr = l & 31;
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  // ---- epilogue: normalised partial O/l as bf16 rows. 1/l of each row comes from
+  //      its score wave; each wave stages its 32*CBW columns of all R rows in its
+  //      own tile buffer ([R rows][4*CBW chunks], chunk ^ (row & 15)) and writes
+  //      them out as contiguous row segments.
+  if (l < 32) s_inv[r_own] = l_run > 0.f ? 1.f / l_run : 0.f;
+  lds_barrier();  // every wave is past the last tile; s_inv complete
+  constexpr int CPR = 4 * CBW;  // 16-byte chunks per staged row
+  constexpr int RSB = 16 * CPR;  // staged row bytes
+  char* stg = w == 0 ? s_tile0 : w == 1 ? s_tile1 : w == 2 ? s_tile2 : s_tile3;
 #pragma unroll
-    for (int cb = 0; cb < 16; ++cb)
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = 32 * rb + (l & 31);
+    const float inv = s_inv[row];
+#pragma unroll
+    for (int cbl = 0; cbl < CBW; ++cbl)
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
-        const int c0 = 32 * cb + 8 * v4;  // this lane holds columns c0 + 4(l/32) .. +3
-        const int chunk = (c0 >> 3) ^ (rr & 15);
-        u32x2 v2 = {pack_bf16x2(acc[cb][4 * v4] * inv, acc[cb][4 * v4 + 1] * inv),
-                    pack_bf16x2(acc[cb][4 * v4 + 2] * inv, acc[cb][4 * v4 + 3] * inv)};
-        *(lds_u32x2*)(lds_ptr(stg) + rr * 1024 + chunk * 16 + (l >> 5) * 8) = v2;
+        const f32x16& o = acc[cbl * RB + rb];
+        const int chunk = (4 * cbl + v4) ^ (row & 15);
+        const u32x2 v2 = {pack_bf16x2(o[4 * v4] * inv, o[4 * v4 + 1] * inv),
+                          pack_bf16x2(o[4 * v4 + 2] * inv, o[4 * v4 + 3] * inv)};
+        *(lds_u32x2*)(lds_ptr(stg) + row * RSB + chunk * 16 + (l >> 5) * 8) = v2;
       }
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging writes are done
   __builtin_amdgcn_wave_barrier();
+  const int64_t part_row0 = (static_cast<int64_t>(b) * a.n_splits + s) * a.n_q;
+  constexpr int RPI = 64 / CPR;  // rows per wave instruction
 #pragma unroll 4
-  for (int q = 0; q < 32; ++q) {
-    const int r = 32 * w + q;
-    const int j = r / HG, head = hg * HG + r % HG;
-    const u32x4 v = *(lds_u32x4*)(lds_ptr(stg) + q * 1024 + ((l ^ (q & 15)) << 4));
-    *reinterpret_cast<u32x4*>(a.o_part + ((part_row0 + j) * a.h + head) * 512 + l * 8) = v;
+  for (int q = 0; q < C::R / RPI; ++q) {
+    const int row = RPI * q + l / CPR, ch = l % CPR;
+    const int j = row / HG, head = hg * HG + row % HG;
+    const u32x4 v = *(lds_u32x4*)(lds_ptr(stg) + row * RSB + ((ch ^ (row & 15)) << 4));
+    *reinterpret_cast<u32x4*>(a.o_part + ((part_row0 + j) * a.h + head) * 512 + 32 * CBW * w + ch * 8) = v;
   }
   if (l < 32) {
     float* ml = a.ml_part + ((part_row0 + j_own) * a.h + head_own) * 2;
@@ -389,19 +459,21 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   }
 }
 
-hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+  // hipExtLaunchKernelGGL stamps ev0/ev1 from the dispatch itself, so an event pair
+  // brackets exactly this kernel's execution (null events: plain launch).
   const int rows = a.h * a.n_q;
   if (rows % 128 == 0) {
     const unsigned units = static_cast<unsigned>(a.batch * a.n_splits * (rows / 128));
     if (a.d_r == 64)
-      decode_kernel<4, 64><<<units, 256, 0, s>>>(a);
+      hipExtLaunchKernelGGL(decode_kernel<4, 64>, dim3(units), dim3(256), 0, s, ev0, ev1, 0, a);
     else
-      decode_kernel<4, 0><<<units, 256, 0, s>>>(a);
+      hipExtLaunchKernelGGL(decode_kernel<4, 0>, dim3(units), dim3(256), 0, s, ev0, ev1, 0, a);
   } else {
     // 64 query rows per workgroup (e.g. 64 heads, one query): position-free rows only
     if (a.d_r != 0) return hipErrorInvalidValue;
     const unsigned units = static_cast<unsigned>(a.batch * a.n_splits * (rows / 64));
-    decode_kernel<2, 0><<<units, 128, 0, s>>>(a);
+    hipExtLaunchKernelGGL(decode_kernel<2, 0>, dim3(units), dim3(128), 0, s, ev0, ev1, 0, a);
   }
   return hipGetLastError();
 }

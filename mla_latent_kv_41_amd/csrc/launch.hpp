@@ -43,7 +43,7 @@ struct DecodeArgs {
   float* ml_part;         // [B][S][n_q][h][2]
   int32_t batch, n_q, h, d_r, n_splits, chunk, max_kv_len;
 };
-hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 
 struct CombineArgs {
   const uint16_t* o_part;  // [B][S][n_q][h][512] bf16
