@@ -92,6 +92,8 @@ struct Ic {
 // compiler's wait insertion does not track it (it would otherwise wait for all
 // such loads before unrelated LDS reads); the kernel bounds these loads with
 // explicit vmcnt waits. M0 (the LDS base) is restored, and no register is written.
+// The target buffer is never read while its loads are in flight, so the statement
+// needs no memory clobber; being volatile, it keeps its order against the barriers.
 __device__ __forceinline__ void dma_b128(const u32x4& rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
   uint32_t saved;
   asm volatile("" : "+s"(soff), "+s"(lds));  // registers, never folded literals
@@ -102,8 +104,22 @@ __device__ __forceinline__ void dma_b128(const u32x4& rsrc, uint32_t voff, uint3
       "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
-      : "memory");
+      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff));
+}
+
+// Score MFMA in VGPR form: Sᵀ += A · B with the accumulator in VGPRs. (The
+// compiler selects the AGPR form for every builtin MFMA of this kernel, whose AGPRs
+// hold the value accumulators.) The leading s_nop gives the 2 wait states a VALU
+// write of an operand needs before an MFMA reads it; back-to-back accumulation into
+// the same registers needs none.
+__device__ __forceinline__ void mfma_v(f32x16& c, const u32x4& a, const u32x4& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+// Last MFMA of a chain: also waits out the 8-pass result latency (> 11 wait states)
+// before any VALU instruction may read or write the accumulator.
+__device__ __forceinline__ void mfma_v_last(f32x16& c, const u32x4& a, const u32x4& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 4"
+      : "+v"(c) : "v"(a), "v"(b));
 }
 
 // s_waitcnt that bounds only the vector-memory counter (lgkm and exp left free).
@@ -180,13 +196,13 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   };
   int pg_next = paged ? page_id(0) : 0;  // block of the next tile to issue, read one issue ahead
 
-  // A 32-token tile never straddles a block (ranges start at multiples of 32 and
-  // blocks are multiples of 32 tokens), so one buffer resource covers the tile;
-  // its size bound keeps every load of the tile inside it. Tiles are issued in
-  // order, so the block of tile it + 1 is fetched while tile it is issued.
-  auto issue_tile = [&](int it, char* tile) __attribute__((always_inline)) {
+  // Buffer resource of tile `it`: base at the tile's first row, size bound covering
+  // only the tile's rows inside the range, so loads of rows past the range end return
+  // zeros (those tokens are masked). A 32-token tile never straddles a block (ranges
+  // start at multiples of 32, blocks hold multiples of 32 tokens). Tiles are taken in
+  // order, so the block of tile it + 1 is fetched here, one tile ahead.
+  auto tile_rsrc = [&](int it) __attribute__((always_inline)) -> u32x4 {
     const int t0 = t_begin + it * kTileT;
-    lds_char* dst = lds_ptr(tile);
     const char* base;
     if (!paged) {
       base = cache + (static_cast<int64_t>(b) * a.cache.t_max + t0) * C::ROWB;
@@ -194,28 +210,24 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       base = cache + (static_cast<int64_t>(pg_next) * a.cache.block_size + t0 % a.cache.block_size) * C::ROWB;
       if (it + 1 < n_tiles) pg_next = page_id(it + 1);
     }
-    // raw buffer resource: base, stride 0, size bound TILE_BYTES
     const uint64_t ba = reinterpret_cast<uint64_t>(base);
-    const u32x4 rsrc = {static_cast<uint32_t>(ba), static_cast<uint32_t>(ba >> 32) & 0xFFFFu,
-                        static_cast<uint32_t>(C::TILE_BYTES), 0x00020000u};
-    const bool full = t0 + kTileT <= t_end;
-    const int last = t_end - 1 - t0;  // rows past it re-read row `last` (masked later)
+    const uint32_t rows = static_cast<uint32_t>(min(kTileT, t_end - t0));
+    return u32x4{static_cast<uint32_t>(ba), static_cast<uint32_t>(ba >> 32) & 0xFFFFu,
+                 rows * static_cast<uint32_t>(C::ROWB), 0x00020000u};
+  };
+  // Load n of this wave's share of a tile: wave load n' = n*NW + w fills LDS
+  // [n'*1024, +1024) from column group n'/4, rows 8(n'%4) .. +7; the whole byte
+  // offset is per lane (soffset 0) so the size bound applies to all of it.
+  auto issue_load = [&](const u32x4& rsrc, char* tile, int n) __attribute__((always_inline)) {
+    const int np = n * NW + w;  // wave-uniform
+    const int G = np >> 2, rq = np & 3;
+    const uint32_t voff = ld_lane[rq & 1] + static_cast<uint32_t>(G * 128 + (rq >> 1) * 16 * C::ROWB);
+    dma_b128(rsrc, voff, 0u, static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_ptr(tile) + np * 1024)));
+  };
+  auto issue_tile = [&](int it, char* tile) __attribute__((always_inline)) {
+    const u32x4 rsrc = tile_rsrc(it);
 #pragma unroll
-    for (int n = 0; n < C::LOADS; ++n) {
-      const int np = n * NW + w;  // wave-uniform
-      const int G = np >> 2, rq = np & 3;
-      // uniform part: group G columns, rows 8*rq (minus the odd-quad base in ld_lane)
-      uint32_t soff = static_cast<uint32_t>(G * 128 + (rq >> 1) * 16 * C::ROWB);
-      uint32_t voff = ld_lane[rq & 1];
-      if (!full) {
-        // the LDS slot keeps its chunk position; its source row is clamped to `last`
-        const int row = 8 * rq + (l >> 3);
-        const uint32_t c16 = voff - static_cast<uint32_t>((8 * (rq & 1) + (l >> 3)) * C::ROWB);
-        voff = static_cast<uint32_t>(min(row, last) * C::ROWB) + c16;
-        soff = static_cast<uint32_t>(G * 128);
-      }
-      dma_b128(rsrc, voff, soff, static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst + np * 1024)));
-    }
+    for (int n = 0; n < C::LOADS; ++n) issue_load(rsrc, tile, n);
   };
 
   // ---- per-lane LDS read offsets
@@ -257,16 +269,23 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   float l_run = 0.f;
   if (tid == 0) s_restart = 0;
 
-  // ---- scores: Sᵀ[32 tokens][32 rows of this wave], four fragments in flight
-  auto scores = [&](const char* tile) __attribute__((always_inline)) {
+  // ---- scores: Sᵀ[32 tokens][32 rows of this wave], SDEPTH fragments in flight
+  constexpr int SDEPTH = 4;
+  auto scores = [&](const char* tile, auto hook) __attribute__((always_inline)) {
     f32x16 sc = {};
-    u32x4 fa[4];
+    u32x4 fa[SDEPTH];
+    // k-step ks: column group ks/4, chunk pair ks%4
+    auto frag = [&](int ks) __attribute__((always_inline)) {
+      return *(lds_u32x4*)(lds_ptr(tile) + sa_off[ks & 3] + (ks >> 2) * 4096);
+    };
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) fa[kk] = *(lds_u32x4*)(lds_ptr(tile) + sa_off[kk]);  // group 0
+    for (int ks = 0; ks < SDEPTH; ++ks) fa[ks] = frag(ks);
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[ks & 3]), as_bf16x8(qf[ks]), sc, 0, 0, 0);
-      if (ks + 4 < C::KS) fa[ks & 3] = *(lds_u32x4*)(lds_ptr(tile) + sa_off[ks & 3] + ((ks + 4) >> 2) * 4096);
+      if (ks + 1 < C::KS) mfma_v(sc, fa[ks % SDEPTH], qf[ks]);
+      else mfma_v_last(sc, fa[ks % SDEPTH], qf[ks]);
+      hook(ks);
+      if (ks + SDEPTH < C::KS) fa[ks % SDEPTH] = frag(ks + SDEPTH);
     }
     return sc;
   };
@@ -278,14 +297,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     u32x4 p[2];
     bool overrun;
   };
-  auto softmax = [&](f32x16 sc, int it, bool allow_restart) __attribute__((always_inline)) {
-    const int t0 = t_begin + it * kTileT;
-    const int lim = min(t_end - 1, vis_own);  // last token this row may see
-    if (t0 + kTileT - 1 > min(t_end - 1, kv - a.n_q)) {
+  auto softmax = [&](bool masked, f32x16 sc, int it, bool allow_restart) __attribute__((always_inline)) {
+    if (masked) {  // uniform
+      const int t0 = t_begin + it * kTileT;
+      const int lim = min(t_end - 1, vis_own);  // last token this row may see
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int tok = t0 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
-        if (tok > lim) sc[v] = -INFINITY;
+        sc[v] = tok > lim ? -INFINITY : sc[v];
       }
     }
     float mx = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
@@ -310,9 +329,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   };
 
   // ---- values for this wave's CBW column blocks and every row block:
-  //      Oᵀ[c][r] += Σ_t Cᵀ[c][t] · Pᵀ[t][r]; P of all rows comes from LDS, the
-  //      2*CBW transposed cache fragments stream through a four-deep window
-  auto pv = [&](const char* tile) __attribute__((always_inline)) {
+  //      Oᵀ[c][r] += Σ_t Cᵀ[c][t] · Pᵀ[t][r]; P of all rows comes from LDS one
+  //      k-step at a time, the 2*CBW transposed cache fragments stream through a
+  //      four-deep window
+  auto pv = [&](const char* tile, auto hook) __attribute__((always_inline)) {
     auto load = [&](int f) __attribute__((always_inline)) {
       const int kk = f / CBW, cb = CBW * w + f % CBW;
       lds_char* tb = lds_ptr(tile) + kk * 16 * 128 + (cb >> 1) * 4096;
@@ -321,24 +341,25 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       const i16x8 af = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       return af;
     };
-    u32x4 pb[2][RB];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) pb[kk][rb] = *(lds_u32x4*)(lds_ptr(s_p) + (rb * 2 + kk) * 1024 + l * 16);
     constexpr int NF = 2 * CBW;
     constexpr int WIN = NF < 4 ? NF : 4;
     i16x8 frag[WIN];
 #pragma unroll
     for (int f = 0; f < WIN; ++f) frag[f] = load(f);
+    u32x4 pb[RB];  // P fragments of the current k-step, one per row block
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const int kk = f / CBW, cbl = f % CBW;
+      if (cbl == 0) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) pb[rb] = *(lds_u32x4*)(lds_ptr(s_p) + (rb * 2 + kk) * 1024 + l * 16);
+      }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
         acc[cbl * RB + rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, frag[f % WIN]), as_bf16x8(pb[kk][rb]), acc[cbl * RB + rb], 0, 0, 0);
+            __builtin_bit_cast(bf16x8, frag[f % WIN]), as_bf16x8(pb[rb]), acc[cbl * RB + rb], 0, 0, 0);
       if (f + WIN < NF) frag[f % WIN] = load(f + WIN);
+      hook(f);
     }
   };
 
@@ -350,27 +371,62 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     else return s_tile3;
   };
 
-  // step i: tile i in buffer i % NBUF; tiles up to i + NBUF - 2 were issued before.
-  // Returns true when some row asked for a restart at tile i.
-  auto step = [&](auto kc, int i, bool allow_restart) __attribute__((always_inline)) -> bool {
-    constexpr int K = decltype(kc)::value;
-    const int ahead = min(n_tiles - 1, i + NBUF - 2) - i;  // tiles issued after tile i
-    if constexpr (NBUF == 4) {
-      if (ahead >= 2) wait_vm<2 * C::LOADS>();
-      else if (ahead == 1) wait_vm<C::LOADS>();
-      else wait_vm<0>();
-    } else {
-      wait_vm<0>();
-    }
-    lds_barrier();  // tile i everywhere; every wave is done with tile i-1 and with P
-    if (i + NBUF - 1 < n_tiles) issue_tile(i + NBUF - 1, tile_ptr(Ic<(K + NBUF - 1) % NBUF>{}));
-    const Soft cur = softmax(scores(tile_ptr(kc)), i, allow_restart);
+  // P of this wave's rows to LDS (B-operand order of the value MFMA) and the
+  // restart request of the tile
+  auto publish = [&](const Soft& cur) __attribute__((always_inline)) {
     *(lds_u32x4*)(lds_ptr(s_p) + (w * 2 + 0) * 1024 + l * 16) = cur.p[0];
     *(lds_u32x4*)(lds_ptr(s_p) + (w * 2 + 1) * 1024 + l * 16) = cur.p[1];
     if (__builtin_amdgcn_ballot_w64(cur.overrun) && l == 0) s_restart = 1;
+  };
+
+  // Tiles from `first_masked` on hold tokens some row must not see (past the end of
+  // the range, or past a row's causal limit); the tiles before it need no mask.
+  const int bound = min(t_end - 1, kv - a.n_q);
+  const int first_masked = bound - t_begin - (kTileT - 1) >= 0 ? (bound - t_begin - (kTileT - 1)) / kTileT + 1 : 0;
+
+  // Wait until at most `ahead` tiles (ahead = 0, 1, 2) of this wave's loads are in flight.
+  auto wait_tiles = [&](int ahead) __attribute__((always_inline)) {
+    if (ahead >= 2) wait_vm<2 * C::LOADS>();
+    else if (ahead == 1) wait_vm<C::LOADS>();
+    else wait_vm<0>();
+  };
+
+  // Step i: scores, softmax and values of tile i (buffer i % NBUF); tiles up to
+  // i + NBUF - 2 were issued before, tile i + NBUF - 1 goes into the buffer of tile
+  // i - 1. Returns true when some row asked for a restart at tile i.
+  auto step = [&](auto kc, int i, bool allow_restart) __attribute__((always_inline)) -> bool {
+    constexpr int K = decltype(kc)::value;
+    if constexpr (NBUF == 4) wait_tiles(min(n_tiles - 1, i + 2) - i);
+    else wait_vm<0>();
+    lds_barrier();  // tile i everywhere; every wave is done with tile i - 1 and P
+    // The loads of tile i + NBUF - 1 go out one at a time, spread over the step: a
+    // CU keeps only about one tile of loads in flight, and a load issued while that
+    // capacity is taken stalls this wave until an earlier one drains.
+    const bool more = i + NBUF - 1 < n_tiles;
+    char* nxt = tile_ptr(Ic<(K + NBUF - 1) % NBUF>{});
+    const u32x4 rs = more ? tile_rsrc(i + NBUF - 1) : u32x4{0u, 0u, 0u, 0u};
+    auto issue_one = [&](int n) __attribute__((always_inline)) {
+      if (more) issue_load(rs, nxt, n);
+    };
+    // load n goes out after score k-step kS(n) or value fragment kV(n)
+    constexpr int NS = (C::LOADS + 1) / 2;  // loads during the scores (after the first)
+    issue_one(0);
+    const f32x16 sc = scores(tile_ptr(kc), [&](int ks) __attribute__((always_inline)) {
+      constexpr int step_ks = C::KS / NS;
+#pragma unroll
+      for (int n = 1; n < NS; ++n)
+        if (ks == n * step_ks - 1) issue_one(n);
+    });
+    publish(softmax(i >= first_masked, sc, i, allow_restart));
     lds_barrier();  // P of every row
     const int restart = s_restart;
-    pv(tile_ptr(kc));
+    pv(tile_ptr(kc), [&](int f) __attribute__((always_inline)) {
+      constexpr int NV = C::LOADS - NS;  // loads during the values
+      constexpr int NF = 2 * CBW;
+#pragma unroll
+      for (int n = 0; n < NV; ++n)
+        if (f == (n * NF) / NV) issue_one(NS + n);
+    });
     return restart != 0;
   };
 
@@ -401,12 +457,15 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     if (pass > 0) prologue();
     bool restart = false;
     for (int i = 0; i < n_tiles && !restart; i += NBUF) {
-      restart = step(Ic<0>{}, i, allow_restart);
-      if (!restart && i + 1 < n_tiles) restart = step(Ic<1>{}, i + 1, allow_restart);
+#define MLA_STEP(KK) \
+  if (!restart && i + KK < n_tiles) restart = step(Ic<KK>{}, i + KK, allow_restart);
+      MLA_STEP(0)
+      MLA_STEP(1)
       if constexpr (NBUF == 4) {
-        if (!restart && i + 2 < n_tiles) restart = step(Ic<2>{}, i + 2, allow_restart);
-        if (!restart && i + 3 < n_tiles) restart = step(Ic<3>{}, i + 3, allow_restart);
+        MLA_STEP(2)
+        MLA_STEP(3)
       }
+#undef MLA_STEP
     }
     wait_vm<0>();  // this wave's loads have landed (a restart leaves some in flight)
     if (!restart) break;
