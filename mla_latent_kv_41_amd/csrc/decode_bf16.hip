@@ -88,23 +88,25 @@ struct Ic {
 };
 
 // One 16-byte-per-lane direct-to-LDS load: lane l's 16 bytes at buffer offset
-// voff + soff land at LDS address lds + 16*l. Issued from asm so that the
+// lane_off + off land at LDS address lds + 16*l. Issued from asm so that the
 // compiler's wait insertion does not track it (it would otherwise wait for all
 // such loads before unrelated LDS reads); the kernel bounds these loads with
-// explicit vmcnt waits. M0 (the LDS base) is restored, and no register is written.
-// The target buffer is never read while its loads are in flight, so the statement
-// needs no memory clobber; being volatile, it keeps its order against the barriers.
-__device__ __forceinline__ void dma_b128(const u32x4& rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
-  uint32_t saved;
-  asm volatile("" : "+s"(soff), "+s"(lds));  // registers, never folded literals
+// explicit vmcnt waits. The offset is formed inside the block (so no per-load
+// offset stays live in a VGPR), M0 (the LDS base) is restored, and the only
+// register written is that temporary. The target buffer is never read while its
+// loads are in flight, so the statement needs no memory clobber; being volatile,
+// it keeps its order against the barriers.
+__device__ __forceinline__ void dma_b128(const u32x4& rsrc, uint32_t lane_off, uint32_t off, uint32_t lds) {
+  uint32_t saved, voff;
+  asm volatile("" : "+s"(off), "+s"(lds));  // registers, never folded literals
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "v_add_u32 %1, %4, %3\n\t"
+      "buffer_load_dwordx4 %1, %5, 0 offen lds\n\t"
       "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff));
+      : "=&s"(saved), "=&v"(voff)
+      : "s"(lds), "v"(lane_off), "s"(off), "s"(rsrc));
 }
 
 // Score MFMA in VGPR form: Sᵀ += A · B with the accumulator in VGPRs. (The
@@ -221,8 +223,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   auto issue_load = [&](const u32x4& rsrc, char* tile, int n) __attribute__((always_inline)) {
     const int np = n * NW + w;  // wave-uniform
     const int G = np >> 2, rq = np & 3;
-    const uint32_t voff = ld_lane[rq & 1] + static_cast<uint32_t>(G * 128 + (rq >> 1) * 16 * C::ROWB);
-    dma_b128(rsrc, voff, 0u, static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_ptr(tile) + np * 1024)));
+    dma_b128(rsrc, ld_lane[rq & 1], static_cast<uint32_t>(G * 128 + (rq >> 1) * 16 * C::ROWB),
+             static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_ptr(tile) + np * 1024)));
   };
   auto issue_tile = [&](int it, char* tile) __attribute__((always_inline)) {
     const u32x4 rsrc = tile_rsrc(it);
@@ -290,42 +292,66 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     return sc;
   };
 
-  // ---- softmax of tile `it` for row r_own against the fixed reference: returns P
-  //      as 8 packed bf16 pairs (values 2k, 2k+1 of the score accumulator) and
-  //      whether a score overran the reference by more than the headroom
+  // ---- softmax of a tile for row r_own against the fixed reference: P as 8 packed
+  //      bf16 pairs (values 2k, 2k+1 of the score accumulator) and whether a score
+  //      overran the reference by more than the headroom. Written as 26 short
+  //      micro-steps (max and reference, one probability each, row sum).
   struct Soft {
     u32x4 p[2];
     bool overrun;
   };
-  auto softmax = [&](bool masked, f32x16 sc, int it, bool allow_restart) __attribute__((always_inline)) {
-    if (masked) {  // uniform
-      const int t0 = t_begin + it * kTileT;
-      const int lim = min(t_end - 1, vis_own);  // last token this row may see
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int tok = t0 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
-        sc[v] = tok > lim ? -INFINITY : sc[v];
-      }
-    }
-    float mx = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
-#pragma unroll
-    for (int v = 3; v < 15; v += 2) mx = fmaxf(fmaxf(mx, sc[v]), sc[v + 1]);
-    mx = half_max(fmaxf(mx, sc[15]));
-    m_seen = fmaxf(m_seen, mx);
-    // first visible tile of the row: nothing accumulated yet, so set the reference
-    if (m_ref == -INFINITY) m_ref = mx;
+  struct SoftState {
+    float mxa[5], t0, t1, mx, mref, pa;
+    float ps[4];
     Soft r;
-    r.overrun = allow_restart && mx > m_ref + kHeadroom;
-    const float mref = m_ref == -INFINITY ? 0.f : m_ref;
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+  };
+  // tokens a row must not see (past the range end or its causal limit) score -inf
+  auto apply_mask = [&](f32x16& sc, int it) __attribute__((always_inline)) {
+    const int t0 = t_begin + it * kTileT;
+    const int lim = min(t_end - 1, vis_own);  // last token this row may see
 #pragma unroll
-    for (int v = 0; v < 16; v += 2) {
-      const float p0 = fast_exp2(sc[v] - mref), p1 = fast_exp2(sc[v + 1] - mref);
-      ps[(v >> 1) & 3] += p0 + p1;
-      r.p[v >> 3][(v >> 1) & 3] = pack_bf16x2(p0, p1);
+    for (int v = 0; v < 16; ++v) {
+      const int tok = t0 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
+      sc[v] = tok > lim ? -INFINITY : sc[v];
     }
-    l_run += half_sum((ps[0] + ps[1]) + (ps[2] + ps[3]));
-    return r;
+  };
+  // micro-steps: 0..8 row max and reference, 9..24 one probability each (a pair is
+  // packed as soon as its second value exists), 25 the row sum
+  constexpr int kSoftSteps = 26;
+  auto soft_step = [&](int k, const f32x16& sc, SoftState& st, bool allow_restart) __attribute__((always_inline)) {
+    if (k < 5) {
+      st.mxa[k] = fmaxf(fmaxf(sc[3 * k], sc[3 * k + 1]), sc[3 * k + 2]);
+    } else if (k == 5) {
+      st.t0 = fmaxf(fmaxf(st.mxa[0], st.mxa[1]), sc[15]);
+    } else if (k == 6) {
+      st.t1 = fmaxf(fmaxf(st.mxa[2], st.mxa[3]), st.mxa[4]);
+    } else if (k == 7) {
+      st.mx = half_max(fmaxf(st.t0, st.t1));
+    } else if (k == 8) {
+      m_seen = fmaxf(m_seen, st.mx);
+      // first visible tile of the row: nothing accumulated yet, so set the reference
+      if (m_ref == -INFINITY) m_ref = st.mx;
+      st.r.overrun = allow_restart && st.mx > m_ref + kHeadroom;
+      st.mref = m_ref == -INFINITY ? 0.f : m_ref;
+    } else if (k < 25) {
+      const int v = k - 9, q = v >> 1;
+      const float pv = fast_exp2(sc[v] - st.mref);
+      if ((v & 1) == 0) {
+        st.pa = pv;
+      } else {
+        st.r.p[q >> 2][q & 3] = pack_bf16x2(st.pa, pv);
+        st.ps[q & 3] = (q < 4 ? 0.f : st.ps[q & 3]) + (st.pa + pv);
+      }
+    } else {
+      l_run += half_sum((st.ps[0] + st.ps[1]) + (st.ps[2] + st.ps[3]));
+    }
+  };
+  auto softmax = [&](bool masked, f32x16 sc, int it, bool allow_restart) __attribute__((always_inline)) {
+    if (masked) apply_mask(sc, it);  // uniform
+    SoftState st;
+#pragma unroll
+    for (int k = 0; k < kSoftSteps; ++k) soft_step(k, sc, st, allow_restart);
+    return st.r;
   };
 
   // ---- values for this wave's CBW column blocks and every row block:
