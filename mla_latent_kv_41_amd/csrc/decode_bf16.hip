@@ -358,7 +358,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   //      Oᵀ[c][r] += Σ_t Cᵀ[c][t] · Pᵀ[t][r]; P of all rows comes from LDS one
   //      k-step at a time, the 2*CBW transposed cache fragments stream through a
   //      four-deep window
-  auto pv = [&](const char* tile, auto hook) __attribute__((always_inline)) {
+  // `mstep(j)` runs after value MFMA j (of 2*CBW*RB); with `pinned`, each MFMA and
+  // its mstep stay together in issue order (VALU work issued while the MFMA runs)
+  auto pv = [&](const char* tile, auto hook, auto mstep, auto pinned) __attribute__((always_inline)) {
     auto load = [&](int f) __attribute__((always_inline)) {
       const int kk = f / CBW, cb = CBW * w + f % CBW;
       lds_char* tb = lds_ptr(tile) + kk * 16 * 128 + (cb >> 1) * 4096;
@@ -381,11 +383,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         for (int rb = 0; rb < RB; ++rb) pb[rb] = *(lds_u32x4*)(lds_ptr(s_p) + (rb * 2 + kk) * 1024 + l * 16);
       }
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
+      for (int rb = 0; rb < RB; ++rb) {
         acc[cbl * RB + rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             __builtin_bit_cast(bf16x8, frag[f % WIN]), as_bf16x8(pb[rb]), acc[cbl * RB + rb], 0, 0, 0);
-      if (f + WIN < NF) frag[f % WIN] = load(f + WIN);
-      hook(f);
+        if (rb == RB - 1 && f + WIN < NF) frag[f % WIN] = load(f + WIN);  // after its last use
+        if (rb == 0) hook(f);
+        mstep(f * RB + rb);
+        if constexpr (decltype(pinned)::value != 0) __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
@@ -452,15 +457,68 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int n = 0; n < NV; ++n)
         if (f == (n * NF) / NV) issue_one(NS + n);
-    });
+    }, [](int) {}, Ic<0>{});
     return restart != 0;
   };
 
+  // Four tile buffers, pipelined on the value side. Step i computes tile i's scores,
+  // then runs tile i's softmax interleaved with the value MFMAs of tile i - 1 (whose P
+  // was published at the end of step i - 1), and publishes P of tile i after every
+  // wave is done with P of tile i - 1. Tiles i and i - 1 are in use, tile i + 1 is in
+  // flight, and tile i + 2 goes into the buffer of tile i - 2. `first` is step 0,
+  // which has no previous tile. Returns true when some row asked for a restart.
+  auto vstep = [&](auto kc, auto first, int i, bool allow_restart) __attribute__((always_inline)) -> bool {
+    constexpr int K = decltype(kc)::value;
+    constexpr bool FIRST = decltype(first)::value != 0;
+    wait_tiles(i + 1 < n_tiles ? 1 : 0);  // tile i has landed
+    lds_barrier();  // tile i and P of tile i - 1 everywhere; tile i - 2 is free
+    const bool more = i + 2 < n_tiles;
+    char* nxt = tile_ptr(Ic<(K + 2) % 4>{});
+    const u32x4 rs = more ? tile_rsrc(i + 2) : u32x4{0u, 0u, 0u, 0u};
+    auto issue_one = [&](int n) __attribute__((always_inline)) {
+      if (more) issue_load(rs, nxt, n);
+    };
+    constexpr int NS = (C::LOADS + 1) / 2;  // loads during the scores (after the first)
+    issue_one(0);
+    f32x16 sc = scores(tile_ptr(kc), [&](int ks) __attribute__((always_inline)) {
+      constexpr int step_ks = C::KS / NS;
+#pragma unroll
+      for (int n = 1; n < NS; ++n)
+        if (ks == n * step_ks - 1) issue_one(n);
+    });
+    if (i >= first_masked) apply_mask(sc, i);  // uniform
+    SoftState st;
+    if constexpr (FIRST) {
+#pragma unroll
+      for (int k = 0; k < kSoftSteps; ++k) soft_step(k, sc, st, allow_restart);
+#pragma unroll
+      for (int n = NS; n < C::LOADS; ++n) issue_one(n);
+    } else {
+      pv(tile_ptr(Ic<(K + 3) % 4>{}), [&](int f) __attribute__((always_inline)) {
+        constexpr int NV = C::LOADS - NS;  // loads during the values
+        constexpr int NF = 2 * CBW;
+#pragma unroll
+        for (int n = 0; n < NV; ++n)
+          if (f == (n * NF) / NV) issue_one(NS + n);
+      }, [&](int j) __attribute__((always_inline)) {
+        if (j < kSoftSteps) soft_step(j, sc, st, allow_restart);
+      }, Ic<1>{});
+    }
+    if (__builtin_amdgcn_ballot_w64(st.r.overrun) && l == 0) s_restart = 1;
+    lds_barrier();  // every wave is done with P of tile i - 1 (and tile i - 1)
+    if (s_restart) return true;
+    *(lds_u32x4*)(lds_ptr(s_p) + (w * 2 + 0) * 1024 + l * 16) = st.r.p[0];
+    *(lds_u32x4*)(lds_ptr(s_p) + (w * 2 + 1) * 1024 + l * 16) = st.r.p[1];
+    return false;
+  };
+
+
   auto prologue = [&]() __attribute__((always_inline)) {
     if (paged) pg_next = page_id(0);
+    constexpr int AHEAD = NBUF == 4 ? 2 : 1;  // tiles issued before the first step
 #pragma unroll
-    for (int k = 0; k < NBUF - 1; ++k)
-      if (k < n_tiles) issue_tile(k, k == 0 ? s_tile0 : k == 1 ? s_tile1 : s_tile2);
+    for (int k = 0; k < AHEAD; ++k)
+      if (k < n_tiles) issue_tile(k, k == 0 ? s_tile0 : s_tile1);
   };
   prologue();
 
@@ -482,16 +540,30 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     l_run = 0.f;
     if (pass > 0) prologue();
     bool restart = false;
-    for (int i = 0; i < n_tiles && !restart; i += NBUF) {
-#define MLA_STEP(KK) \
-  if (!restart && i + KK < n_tiles) restart = step(Ic<KK>{}, i + KK, allow_restart);
-      MLA_STEP(0)
-      MLA_STEP(1)
-      if constexpr (NBUF == 4) {
-        MLA_STEP(2)
-        MLA_STEP(3)
+    if constexpr (NBUF == 4) {
+      restart = vstep(Ic<0>{}, Ic<1>{}, 0, allow_restart);
+      for (int i = 1; i < n_tiles && !restart; i += 4) {
+#define MLA_VSTEP(KK, D) \
+  if (!restart && i + D < n_tiles) restart = vstep(Ic<KK>{}, Ic<0>{}, i + D, allow_restart);
+        MLA_VSTEP(1, 0)
+        MLA_VSTEP(2, 1)
+        MLA_VSTEP(3, 2)
+        MLA_VSTEP(0, 3)
+#undef MLA_VSTEP
       }
-#undef MLA_STEP
+      if (!restart) {
+        lds_barrier();  // P of the last tile everywhere
+        // the value MFMAs of the last tile, from buffer (n_tiles - 1) % 4 (one copy of
+        // the code: a branch per buffer would split the accumulators' registers)
+        const int kl = (n_tiles - 1) & 3;
+        const char* lt = kl == 0 ? s_tile0 : kl == 1 ? s_tile1 : kl == 2 ? s_tile2 : s_tile3;
+        pv(lt, [](int) {}, [](int) {}, Ic<0>{});
+      }
+    } else {
+      for (int i = 0; i < n_tiles && !restart; i += 2) {
+        restart = step(Ic<0>{}, i, allow_restart);
+        if (!restart && i + 1 < n_tiles) restart = step(Ic<1>{}, i + 1, allow_restart);
+      }
     }
     wait_vm<0>();  // this wave's loads have landed (a restart leaves some in flight)
     if (!restart) break;
