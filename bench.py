@@ -7,7 +7,8 @@ d_qk_nope=d_v=128, batch 32, 4096 cached tokens + 1 query token per sequence
 synthetic inputs. One step = one mla_decode call: query absorption + RoPE,
 split-K attention over the latent cache, split combine + W_UV up-projection.
 
-Prints one JSON line. Inputs are resident in HBM before the timed region. Three
+Prints one JSON line. Inputs are resident in HBM before the timed region; untimed
+steps run for half a second (clock settling) before the W warmup steps. Three
 copies of (cache, packed weights) are used in turn, as three layers would be,
 so the 256 MB Infinity Cache cannot hold the working set between steps.
 
@@ -29,6 +30,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2516.6   # dense bf16 matrix-core peak (256 CU x 2.4 GHz x 4096)
 COPIES = 3
+EVERY = 8  # timed steps per sampled attention-kernel event pair
+SETTLE_S = 0.5  # seconds of untimed steps before the warmup steps
 
 
 def log(*a):
@@ -146,7 +149,22 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    ev = HipEvents(args.steps)
+    # The attention kernel is timed on every EVERY-th step of the timed region (at
+    # least four samples): each timed launch carries its own event pair, which costs
+    # the step several microseconds, so sampling keeps the step rate honest.
+    every = max(1, min(EVERY, args.steps // 4))
+    sampled = list(range(0, args.steps, every))
+    ev = HipEvents(len(sampled))
+    # Clock settling: the GPU ramps its clocks over the first fraction of a second of
+    # sustained load, so untimed steps run for SETTLE_S of wall time before the W
+    # warmup steps (measured: 10 warmup steps alone leave the step ~10% slower).
+    t0 = time.perf_counter()
+    k = 0
+    while time.perf_counter() - t0 < SETTLE_S:
+        for _ in range(64):
+            steps[k % COPIES].decode()
+            k += 1
+        torch.cuda.synchronize()
     for k in range(args.warmup):
         steps[k % COPIES].decode()
     torch.cuda.synchronize()
@@ -154,12 +172,15 @@ def main():
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for k in range(args.steps):
-        steps[k % COPIES].decode(events=ev.pairs[k])
+        if k % every == 0:
+            steps[k % COPIES].decode(events=ev.pairs[k // every])
+        else:
+            steps[k % COPIES].decode()
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms = total_ms / args.steps
-    attn_ms = [ev.elapsed_ms(k) for k in range(args.steps)]
+    attn_ms = [ev.elapsed_ms(k) for k in range(len(sampled))]
     attn_avg = float(np.mean(attn_ms))
 
     flops, cache_bytes, alg_bytes = algorithmic(w)
@@ -192,6 +213,7 @@ def main():
         "tflops_frac_of_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "tokens_per_s": round(tok_s, 1),
         "attention_kernel_ms": round(attn_avg, 5),
+        "attention_kernel_samples": len(sampled),
         "roofline": {"bound": "hbm", "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,

@@ -215,6 +215,7 @@ mla_status decode_impl(const mla_dims* dims, const CacheRef& cache, const mla_de
   q.h = r.h;
   q.d_r = r.d_r;
   q.max_kv_len = a->max_kv_len;
+  q.rows_per_wg = 32 * p.nw;
   q.qscale = qscale;
   for (int k = 0; k < r.d_r / 2 && k < 32; ++k) q.inv_freq[k] = pow(r.rope_base, -2.0 * k / r.d_r);
   if (launch_qprep_bf16(q, stream) != hipSuccess) return MLA_E_HIP;

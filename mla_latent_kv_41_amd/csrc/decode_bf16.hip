@@ -526,10 +526,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   //      loaded while the first tiles are in flight; the wait covers both, so no
   //      later wait for these loads lands inside the tile loop
   {
-    const int64_t m = static_cast<int64_t>(b) * a.n_q + j_own;
-    const u32x4* qp = reinterpret_cast<const u32x4*>(a.q_cat + (m * a.h + head_own) * C::ROW) + (l >> 5);
+    // Q_cat is stored in this kernel's fragment order: one 1 KiB wave load per k-step
+    const u32x4* qp = reinterpret_cast<const u32x4*>(a.q_cat) +
+                      ((static_cast<int64_t>(b) * hgroups + hg) * NW + w) * C::KS * 64 + l;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) qf[ks] = qp[2 * ks];
+    for (int ks = 0; ks < C::KS; ++ks) qf[ks] = qp[ks * 64];
   }
   wait_vm<0>();
 

@@ -28,8 +28,9 @@ struct QPrepArgs {
   const uint16_t* q_rope;   // [M][h][64] or nullptr
   const uint16_t* w_uk_pk;  // packed W_UK
   const int32_t* kv_lens;
-  uint16_t* q_cat;          // [M][h][row]
+  uint16_t* q_cat;          // fragment order of the attention kernel (see qprep_kernel)
   int32_t M, n_q, h, d_r, max_kv_len;
+  int32_t rows_per_wg;      // query rows per attention workgroup (32 per wave)
   float qscale;             // scale * log2(e)
   double inv_freq[32];      // rope_base^(-2k/d_r), computed on the host in fp64
 };
@@ -38,7 +39,7 @@ hipError_t launch_qprep_bf16(const QPrepArgs& a, hipStream_t s);
 struct DecodeArgs {
   CacheRef cache;
   const int32_t* kv_lens;
-  const uint16_t* q_cat;  // [M][h][row]
+  const uint16_t* q_cat;  // fragment order (written by qprep_kernel)
   uint16_t* o_part;       // [B][S][n_q][h][512] bf16, normalised O / l
   float* ml_part;         // [B][S][n_q][h][2]
   int32_t batch, n_q, h, d_r, n_splits, chunk, max_kv_len;

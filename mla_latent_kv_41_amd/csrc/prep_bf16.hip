@@ -54,9 +54,26 @@ hipError_t launch_pack_bf16(const uint16_t* w_uk, const uint16_t* w_uv, uint16_t
   return hipGetLastError();
 }
 
+// Q_cat is written in the attention kernel's B-fragment order, so each of its
+// fragment loads is one contiguous 1 KiB wave read: element (row m, head i,
+// column c) sits in workgroup (b, hg) = (m / n_q, i / HG) with HG = R / n_q heads
+// per workgroup of R rows, at row r = (m % n_q) HG + i % HG, wave r / 32, k-step
+// c / 16, lane (r % 32) + 32 ((c / 8) % 2), element c % 8.
+__device__ __forceinline__ int64_t qfrag_off(const QPrepArgs& a, int m, int i, int c) {
+  const int KS = (512 + a.d_r) / 16;
+  const int HG = a.rows_per_wg / a.n_q;
+  const int hgroups = a.h / HG;
+  const int nw = a.rows_per_wg / 32;
+  const int b = m / a.n_q, j = m % a.n_q;
+  const int hg = i / HG, r = j * HG + i % HG;
+  const int lane = (r & 31) + 32 * ((c >> 3) & 1);
+  return ((((static_cast<int64_t>(b) * hgroups + hg) * nw + (r >> 5)) * KS + (c >> 4)) * 64 + lane) * 8 + (c & 7);
+}
+
 // grid (h, 4): head i, quarter cq of the 512 latent columns; 4 waves, wave w owns
 // the 32 columns of block nb = 4cq + w and loops over 32-row blocks of M. The
-// 32 x 128 bf16 result block is staged in LDS so Q_cat is written in 256-byte rows.
+// 32 x 128 bf16 result block is staged in LDS and written out as 16-byte chunks in
+// the fragment order above.
 __global__ __launch_bounds__(256) void qprep_kernel(QPrepArgs a) {
   constexpr int kStride = 128 * 2 + 16;  // bytes per staged row (padded)
   __shared__ __attribute__((aligned(16))) char s_q[32 * kStride];
@@ -64,7 +81,6 @@ __global__ __launch_bounds__(256) void qprep_kernel(QPrepArgs a) {
   const int tid = threadIdx.x, l = tid % 64;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64);
   const int nb = 4 * cq + w;
-  const int row = 512 + a.d_r;
   const u32x4* wk = reinterpret_cast<const u32x4*>(a.w_uk_pk) + ((static_cast<int64_t>(i) * 16 + nb) * 8) * 64 + l;
   u32x4 bfr[8];
 #pragma unroll
@@ -95,7 +111,7 @@ __global__ __launch_bounds__(256) void qprep_kernel(QPrepArgs a) {
       const int m = 32 * mb + r;
       if (m < a.M) {
         const u32x4 v = *(lds_u32x4*)(lds_ptr(s_q) + r * kStride + ch * 16);
-        *reinterpret_cast<u32x4*>(a.q_cat + (static_cast<int64_t>(m) * a.h + i) * row + 128 * cq + ch * 8) = v;
+        *reinterpret_cast<u32x4*>(a.q_cat + qfrag_off(a, m, i, 128 * cq + ch * 8)) = v;
       }
     }
   }
@@ -114,9 +130,9 @@ __global__ __launch_bounds__(256) void qprep_kernel(QPrepArgs a) {
     sincosf(static_cast<float>(red), &sn, &cs);
     const uint16_t* qr = a.q_rope + (static_cast<int64_t>(m) * a.h + i) * a.d_r;
     const float x0 = bf16_bits_to_f32(qr[2 * k]), x1 = bf16_bits_to_f32(qr[2 * k + 1]);
-    uint16_t* dst = a.q_cat + (static_cast<int64_t>(m) * a.h + i) * row + 512;
-    dst[2 * k] = f32_to_bf16_bits((x0 * cs - x1 * sn) * a.qscale);
-    dst[2 * k + 1] = f32_to_bf16_bits((x0 * sn + x1 * cs) * a.qscale);
+    uint16_t* dst = a.q_cat + qfrag_off(a, m, i, 512 + 2 * k);  // columns 512+2k, 513+2k share a chunk
+    dst[0] = f32_to_bf16_bits((x0 * cs - x1 * sn) * a.qscale);
+    dst[1] = f32_to_bf16_bits((x0 * sn + x1 * cs) * a.qscale);
   }
 }
 
