@@ -56,8 +56,8 @@ struct Plan {
   int hgroups;   // workgroups per (sequence, split)
   int n_splits;  // token ranges per sequence
   int chunk;     // tokens per range, a multiple of kTile
-  int comb_rows;    // combine: query rows per workgroup (power of two, <= 16)
-  int comb_splits;  // combine: partial rows staged per row and batch
+  int comb_rows;    // combine: query rows per workgroup (<= 32)
+  int comb_splits;  // combine: partial half rows staged per row and batch
 };
 
 Plan plan_bf16(const Resolved& r, const mla_decode_args* a) {
@@ -88,11 +88,12 @@ Plan plan_bf16(const Resolved& r, const mla_decode_args* a) {
   chunk = (chunk + kTile - 1) / kTile * kTile;
   p.chunk = static_cast<int>(chunk);
   p.n_splits = static_cast<int>((L + chunk - 1) / chunk);
-  // combine grid: (h, M / rows); halve the rows until the grid fills the CUs
+  // combine grid: (h, 2 latent halves, M / rows); halve the rows until the grid fills
+  // the CUs; splits staged per batch fill the 256 half-row slots
   const int M = a->batch * a->n_q;
-  p.comb_rows = 16;
-  while (p.comb_rows > 1 && static_cast<int64_t>(r.h) * ((M + p.comb_rows - 1) / p.comb_rows) < 256) p.comb_rows /= 2;
-  p.comb_splits = std::min(p.n_splits, 128 / p.comb_rows);
+  p.comb_rows = std::min(32, M);
+  while (p.comb_rows > 1 && 2LL * r.h * ((M + p.comb_rows - 1) / p.comb_rows) < 256) p.comb_rows = (p.comb_rows + 1) / 2;
+  p.comb_splits = std::min(p.n_splits, 256 / p.comb_rows);
   return p;
 }
 
@@ -216,6 +217,7 @@ mla_status decode_impl(const mla_dims* dims, const CacheRef& cache, const mla_de
   q.d_r = r.d_r;
   q.max_kv_len = a->max_kv_len;
   q.rows_per_wg = 32 * p.nw;
+  q.out = a->out;  // zeroed here: the combine adds its two latent halves into it
   q.qscale = qscale;
   for (int k = 0; k < r.d_r / 2 && k < 32; ++k) q.inv_freq[k] = pow(r.rope_base, -2.0 * k / r.d_r);
   if (launch_qprep_bf16(q, stream) != hipSuccess) return MLA_E_HIP;

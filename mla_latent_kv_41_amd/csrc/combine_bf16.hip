@@ -16,18 +16,26 @@ namespace mla {
 
 namespace {
 constexpr int kGateSplit = 16;          // K-splits of the gate GEMM
-constexpr int kAStride = 512 * 2 + 16;  // bytes per o_lat row in LDS (padded)
-constexpr int kPartSlots = 128;         // 1 KiB partial rows staged per batch
+constexpr int kHalf = 256;              // latent columns per workgroup (half of d_c)
+constexpr int kSlotBytes = kHalf * 2;   // one staged half partial row (bf16)
+constexpr int kSlots = 256;             // staged half rows per batch (128 KiB)
+constexpr int kAStride = kHalf * 2 + 16;  // bytes per o_lat half row in LDS (padded)
 }  // namespace
 
-// grid (h, ceil(M / rows_per_wg)), 256 threads. Workgroup (i, mb) produces
-// out[m][i*128 .. i*128+127] for rows m in [mb*RPW, mb*RPW + RPW).
+// grid (h, 2, ceil(M / rows_per_wg)), 256 threads. Workgroup (i, kh, mb) takes head i,
+// latent columns [256 kh, 256 kh + 256) and query rows m in [mb R, mb R + R), R <= 32,
+// and adds its share of the up-projection,
+//   out[m][i*128 + d] += Σ_{c in half kh} o_lat[m][i][c] · W_UV_i[c][d],
+// into the output with fp32 atomics (the output was zeroed by the query preparation of
+// the same call). Each output element gets exactly two addends onto zero, so the sum
+// does not depend on their order. Splitting the latent dimension, not the rows, reads
+// each partial row and each W_UV_i once.
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-  __shared__ __attribute__((aligned(1024))) char s_part[kPartSlots * 1024];
-  __shared__ float s_stat[16][2];  // per row: max M and 1 / L
-  __shared__ int s_ns[16];         // per row: number of splits
-  __shared__ float s_w[kPartSlots];  // weight of each staged partial row
-  const int i = blockIdx.x, mb = blockIdx.y;
+  __shared__ __attribute__((aligned(1024))) char s_part[kSlots * kSlotBytes];
+  __shared__ float s_w[kSlots];  // weight of each staged half row
+  __shared__ int s_ns[32];       // per row: number of splits holding its tokens
+  __shared__ float s_stat[32][2];  // per row: max M and 1 / L
+  const int i = blockIdx.x, kh = blockIdx.y, mb = blockIdx.z;
   const int tid = threadIdx.x, l = tid % 64;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64);
   const int M = a.batch * a.n_q;
@@ -35,121 +43,162 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int m0 = mb * RPW;
   const int rows = min(RPW, M - m0);
 
-  // W_UV_i fragments of this wave's 32 output columns, fetched up front
-  const u32x4* wv = reinterpret_cast<const u32x4*>(a.w_uv_pk) + ((static_cast<int64_t>(i) * 4 + w) * 32) * 64 + l;
-  u32x4 bfr[32];
-#pragma unroll
-  for (int ks = 0; ks < 32; ++ks) bfr[ks] = wv[ks * 64];
-
   auto part_row = [&](int m, int sp) -> int64_t {  // row index of split sp of query row m, head i
     const int b = m / a.n_q, j = m % a.n_q;
     return ((static_cast<int64_t>(b) * a.n_splits + sp) * a.n_q + j) * a.h + i;
   };
-
-  // ---- per row (one wave per row): split count, M = max_s m_s, L = Σ_s 2^(m_s - M) l_s
-  for (int r = w; r < rows; r += 4) {
-    const int m = m0 + r, b = m / a.n_q;
-    const int kv = min(a.kv_lens[b], a.max_kv_len);
-    const int ns = kv >= a.n_q ? min((kv + a.chunk - 1) / a.chunk, a.n_splits) : 0;
-    float mx = -INFINITY;
-    for (int sp = l; sp < ns; sp += 64) mx = fmaxf(mx, a.ml_part[part_row(m, sp) * 2]);
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    const float mref = mx == -INFINITY ? 0.f : mx;
-    float L = 0.f;
-    for (int sp = l; sp < ns; sp += 64) {
-      const int64_t pr = part_row(m, sp);
-      L += fast_exp2(a.ml_part[pr * 2] - mref) * a.ml_part[pr * 2 + 1];
-    }
-    for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
-    if (l == 0) {
-      s_stat[r][0] = mref;
-      s_stat[r][1] = L > 0.f ? 1.f / L : 0.f;
-      s_ns[r] = ns;
-      if (a.lse) a.lse[static_cast<int64_t>(m) * a.h + i] = L > 0.f ? (mx + __log2f(L)) * kLn2 : -INFINITY;
-    }
+  if (tid < rows) {
+    const int kv = min(a.kv_lens[(m0 + tid) / a.n_q], a.max_kv_len);
+    s_ns[tid] = kv >= a.n_q ? min((kv + a.chunk - 1) / a.chunk, a.n_splits) : 0;
   }
   __syncthreads();
+
+  // ---- loads in the order they are needed: (m_s, l_s) of this wave's rows (rows w,
+  //      w+4, ...; lane = split), then the W_UV_i fragments of this wave's 32 output
+  //      columns for the 16 k-steps of half kh. Staging of the partial rows follows the
+  //      statistics, so their weights are ready when the rows land.
+  float2 ml0[8];
+  int nsr[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int r = w + 4 * k;
+    nsr[k] = r < rows ? s_ns[r] : 0;
+    ml0[k] = l < nsr[k] ? *reinterpret_cast<const float2*>(a.ml_part + part_row(m0 + r, l) * 2)
+                        : make_float2(-INFINITY, 0.f);
+  }
+  const u32x4* wv = reinterpret_cast<const u32x4*>(a.w_uv_pk) + ((static_cast<int64_t>(i) * 4 + w) * 32 + 16 * kh) * 64 + l;
+  u32x4 bfr[16];
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) bfr[ks] = wv[ks * 64];
+
+  // ---- per row (one wave per row): M = max_s m_s, L = Σ_s 2^(m_s - M) l_s, the
+  //      weights 2^(m_s - M) l_s / L of the first batch, lse. The eight rows of a wave
+  //      are reduced together, so each cross-lane step has eight independent shuffles.
+  float mx[8], L[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    mx[k] = ml0[k].x;
+    const int r = w + 4 * k;
+    for (int sp = l + 64; sp < nsr[k]; sp += 64) mx[k] = fmaxf(mx[k], a.ml_part[part_row(m0 + r, sp) * 2]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) mx[k] = fmaxf(mx[k], __shfl_xor(mx[k], o));
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float mref = mx[k] == -INFINITY ? 0.f : mx[k];
+    L[k] = l < nsr[k] ? fast_exp2(ml0[k].x - mref) * ml0[k].y : 0.f;
+    const int r = w + 4 * k;
+    for (int sp = l + 64; sp < nsr[k]; sp += 64) {
+      const int64_t pr = part_row(m0 + r, sp);
+      L[k] += fast_exp2(a.ml_part[pr * 2] - mref) * a.ml_part[pr * 2 + 1];
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) L[k] += __shfl_xor(L[k], o);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int r = w + 4 * k;
+    if (r >= rows) continue;
+    const int m = m0 + r, ns = nsr[k];
+    const float mref = mx[k] == -INFINITY ? 0.f : mx[k];
+    for (int sp = l; sp < SB; sp += 64) {
+      float wgt = 0.f;
+      if (sp < ns && L[k] > 0.f) {
+        const float2 v = sp < 64 ? ml0[k] : *reinterpret_cast<const float2*>(a.ml_part + part_row(m, sp) * 2);
+        wgt = fast_exp2(v.x - mref) * v.y / L[k];
+      }
+      s_w[r * SB + sp] = wgt;
+    }
+    if (l == 0) {
+      s_stat[r][0] = mref;
+      s_stat[r][1] = L[k] > 0.f ? 1.f / L[k] : 0.f;
+      if (kh == 0 && a.lse) a.lse[static_cast<int64_t>(m) * a.h + i] = L[k] > 0.f ? (mx[k] + __log2f(L[k])) * kLn2 : -INFINITY;
+    }
+  }
   int ns_max = 0;
   for (int r = 0; r < rows; ++r) ns_max = max(ns_max, s_ns[r]);
 
-  // ---- o_lat rows: Σ_s 2^(m_s - M) l_s / L · (O_s / l_s); lane owns 8 columns of
-  //      the rows r = w, w+4, ... (at most 4 per wave)
+  // ---- o_lat half rows: Σ_s w_s (O_s / l_s). A wave takes two rows per pass (lanes
+  //      0-31 row w + 8p, lanes 32-63 row w + 8p + 4), a lane 8 columns.
   float o[4][8];
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
+  for (int p = 0; p < 4; ++p)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[k][e] = 0.f;
+    for (int e = 0; e < 8; ++e) o[p][e] = 0.f;
+  const int hl = l >> 5, cl = l & 31;
   for (int s0 = 0; s0 < ns_max; s0 += SB) {
-    // stage partial rows (r, s0 + q) into LDS slot r*SB + q (one 1 KiB wave load
-    // each) and their weights into s_w[slot] (one thread each); all loads issue
-    // before the single wait
-    for (int slot = w; slot < rows * SB; slot += 4) {
-      const int r = slot / SB, sp = s0 + slot % SB;
-      if (sp < s_ns[r])
-        __builtin_amdgcn_global_load_lds(a.o_part + part_row(m0 + r, sp) * 512 + l * 8,
-                                         (lds_void*)(lds_ptr(s_part) + slot * 1024), 16, 0, 0);
-    }
-    for (int slot = tid; slot < rows * SB; slot += 256) {
-      const int r = slot / SB, sp = s0 + slot % SB;
-      float wgt = 0.f;
-      if (sp < s_ns[r]) {
-        const int64_t pr = part_row(m0 + r, sp);
-        wgt = fast_exp2(a.ml_part[pr * 2] - s_stat[r][0]) * a.ml_part[pr * 2 + 1] * s_stat[r][1];
+    if (s0 > 0) {
+      __syncthreads();  // every wave is done with the previous batch
+      for (int slot = tid; slot < rows * SB; slot += 256) {  // later batches: weights
+        const int r = slot / SB, sp = s0 + slot % SB;
+        float wgt = 0.f;
+        if (sp < s_ns[r]) {
+          const int64_t pr = part_row(m0 + r, sp);
+          wgt = fast_exp2(a.ml_part[pr * 2] - s_stat[r][0]) * a.ml_part[pr * 2 + 1] * s_stat[r][1];
+        }
+        s_w[slot] = wgt;
       }
-      s_w[slot] = wgt;
+    }
+    // stage half rows (r, s0 + q) into slot r*SB + q: one wave load covers two slots
+    for (int pair = w; pair * 2 < rows * SB; pair += 4) {
+      const int slot = pair * 2 + hl;
+      const int r = slot / SB, sp = s0 + slot % SB;
+      if (slot < rows * SB && sp < s_ns[r])
+        __builtin_amdgcn_global_load_lds(a.o_part + part_row(m0 + r, sp) * 512 + kh * kHalf + cl * 8,
+                                         (lds_void*)(lds_ptr(s_part) + pair * 2 * kSlotBytes), 16, 0, 0);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int r = w + 4 * k;
-      if (r >= rows) break;
-      const int nq = min(SB, s_ns[r] - s0);
+    for (int p = 0; p < 4; ++p) {
+      const int r = w + 8 * p + 4 * hl;
+      if (w + 8 * p >= rows) break;
+      const int nq = r < rows ? min(SB, s_ns[r] - s0) : 0;
       for (int q = 0; q < nq; ++q) {
         const float wgt = s_w[r * SB + q];
-        const u32x4 v = *(lds_u32x4*)(lds_ptr(s_part) + (r * SB + q) * 1024 + l * 16);
+        const u32x4 v = *(lds_u32x4*)(lds_ptr(s_part) + (r * SB + q) * kSlotBytes + cl * 16);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          o[k][2 * e] += wgt * __uint_as_float(v[e] << 16);
-          o[k][2 * e + 1] += wgt * __uint_as_float(v[e] & 0xFFFF0000u);
+          o[p][2 * e] += wgt * __uint_as_float(v[e] << 16);
+          o[p][2 * e + 1] += wgt * __uint_as_float(v[e] & 0xFFFF0000u);
         }
       }
     }
-    __syncthreads();
   }
+  __syncthreads();  // every wave is done with the staged rows
 
   // ---- o_lat as a hi + lo pair of bf16 rows (hi = bf16(o), lo = bf16(o - hi)), so
-  //      the up-projection keeps about 16 significant bits of o_lat
+  //      the up-projection keeps about 16 significant bits of o_lat; rows past
+  //      `rows` are zero
   char* s_hi = s_part;
   char* s_lo = s_part + 32 * kAStride;
-  for (int r = w; r < 32; r += 4) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int r = w + 8 * p + 4 * hl;
     u32x4 hv = {0u, 0u, 0u, 0u}, lv = {0u, 0u, 0u, 0u};
     if (r < rows) {
-      const int k = r >> 2;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float x0 = 0.f, x1 = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          if (kk == k) {
-            x0 = o[kk][2 * e];
-            x1 = o[kk][2 * e + 1];
-          }
+        const float x0 = o[p][2 * e], x1 = o[p][2 * e + 1];
         const uint32_t h2 = pack_bf16x2(x0, x1);
         hv[e] = h2;
         lv[e] = pack_bf16x2(x0 - __uint_as_float(h2 << 16), x1 - __uint_as_float(h2 & 0xFFFF0000u));
       }
     }
-    *(lds_u32x4*)(lds_ptr(s_hi) + r * kAStride + l * 16) = hv;
-    *(lds_u32x4*)(lds_ptr(s_lo) + r * kAStride + l * 16) = lv;
+    *(lds_u32x4*)(lds_ptr(s_hi) + r * kAStride + cl * 16) = hv;
+    *(lds_u32x4*)(lds_ptr(s_lo) + r * kAStride + cl * 16) = lv;
   }
   __syncthreads();
 
-  // ---- out[m][i*128 + 32w + ..] = (o_hi + o_lo)[m][:] · W_UV_i[:, 32w + ..]
+  // ---- out[m][i*128 + 32w + ..] += (o_hi + o_lo)[m][half kh] · W_UV_i[half kh][32w + ..]
   f32x16 acc = {};
   const int arow = (l & 31) * kAStride + (l >> 5) * 16;
 #pragma unroll
-  for (int ks = 0; ks < 32; ++ks) {
+  for (int ks = 0; ks < 16; ++ks) {
     const u32x4 ah = *(lds_u32x4*)(lds_ptr(s_hi) + arow + ks * 32);
     const u32x4 al = *(lds_u32x4*)(lds_ptr(s_lo) + arow + ks * 32);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ah), as_bf16x8(bfr[ks]), acc, 0, 0, 0);
@@ -163,20 +212,20 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     if (r >= rows) continue;
     const int m = m0 + r;
     float ov = acc[v];
-    if (a.gate) {
+    if (a.gate) {  // out = sigmoid(g) (o_0 + o_1): each half carries its factor
       float g = 0.f;
       for (int ks = 0; ks < kGateSplit; ++ks) g += a.gate[(static_cast<int64_t>(ks) * M + m) * width + col];
       ov *= 1.f / (1.f + __expf(-g));
     }
-    a.out[static_cast<int64_t>(m) * width + col] = ov;
+    atomicAdd(a.out + static_cast<int64_t>(m) * width + col, ov);
   }
 }
 
 hipError_t launch_combine_bf16(const CombineArgs& a, hipStream_t s) {
   const int M = a.batch * a.n_q;
-  if (a.rows_per_wg < 1 || a.rows_per_wg > 16 || a.rows_per_wg * a.splits_per_batch > kPartSlots)
+  if (a.rows_per_wg < 1 || a.rows_per_wg > 32 || a.rows_per_wg * a.splits_per_batch > kSlots)
     return hipErrorInvalidValue;
-  combine_kernel<<<dim3(a.h, (M + a.rows_per_wg - 1) / a.rows_per_wg), 256, 0, s>>>(a);
+  combine_kernel<<<dim3(a.h, 2, (M + a.rows_per_wg - 1) / a.rows_per_wg), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -31,6 +31,7 @@ struct QPrepArgs {
   uint16_t* q_cat;          // fragment order of the attention kernel (see qprep_kernel)
   int32_t M, n_q, h, d_r, max_kv_len;
   int32_t rows_per_wg;      // query rows per attention workgroup (32 per wave)
+  float* out;               // [M][h*128] output, zeroed for the combine's atomic adds
   float qscale;             // scale * log2(e)
   double inv_freq[32];      // rope_base^(-2k/d_r), computed on the host in fp64
 };
@@ -52,11 +53,11 @@ struct CombineArgs {
   const int32_t* kv_lens;
   const uint16_t* w_uv_pk;  // packed W_UV
   const float* gate;        // [M][h*128] pre-activation gate logits or nullptr
-  float* out;               // [M][h*128]
+  float* out;               // [M][h*128], zeroed beforehand: halves are added atomically
   float* lse;               // [M][h] or nullptr
   int32_t batch, n_q, h, n_splits, chunk, max_kv_len;
-  int32_t rows_per_wg;       // query rows per workgroup, 1..16
-  int32_t splits_per_batch;  // partial rows staged per row and batch (rows * splits <= 128)
+  int32_t rows_per_wg;       // query rows per workgroup, 1..32
+  int32_t splits_per_batch;  // half partial rows staged per row and batch (rows * splits <= 256)
 };
 hipError_t launch_combine_bf16(const CombineArgs& a, hipStream_t s);
 

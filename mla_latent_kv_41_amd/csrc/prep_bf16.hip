@@ -79,6 +79,9 @@ __global__ __launch_bounds__(256) void qprep_kernel(QPrepArgs a) {
   __shared__ __attribute__((aligned(16))) char s_q[32 * kStride];
   const int i = blockIdx.x, cq = blockIdx.y;
   const int tid = threadIdx.x, l = tid % 64;
+  // zero this head's quarter of the output columns (the combine adds into them)
+  for (int idx = tid; idx < a.M * 32; idx += blockDim.x)
+    a.out[static_cast<int64_t>(idx / 32) * a.h * 128 + i * 128 + 32 * cq + idx % 32] = 0.f;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64);
   const int nb = 4 * cq + w;
   const u32x4* wk = reinterpret_cast<const u32x4*>(a.w_uk_pk) + ((static_cast<int64_t>(i) * 16 + nb) * 8) * 64 + l;
