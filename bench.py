@@ -114,6 +114,108 @@ def cpu_baseline(w, t, budget_s=12.0):
             "sample": "%d of %d sequences (all %d heads), fp64 explicit-K/V oracle, %.1f s; "
                       "query tokens/s %.3g" % (done, w.batch, w.h, secs, done * w.n_q / secs)}
 
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out>/prof_ds -o ds -- "
+             "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline")
+PMC_CMD = ("rocprofv3 --pmc {c} --output-format csv -d <out>/pmc/{c} -o {c} -- "
+           "python3 bench.py --steps 4 --warmup 2 --no-cpu-baseline --calibrate-copy")
+COPY_BYTES = 512 << 20
+
+
+def _bench_line(log_path):
+    """The JSON line a profiled bench run printed (its last line starting with '{')."""
+    line = None
+    for ln in open(log_path):
+        if ln.startswith("{"):
+            line = ln
+    if line is None:
+        raise SystemExit("no bench result line in %s" % log_path)
+    return json.loads(line)
+
+
+def summarize_profiles(d):
+    """Summaries of a kernel-trace run (DIR/prof_ds, log DIR/prof_ds.log) and of one
+    FETCH_SIZE and one WRITE_SIZE counter run (DIR/pmc/<C>, logs DIR/pmc/<C>.log) of
+    this bench: the per-kernel table, the counter table with the 512 MiB copy
+    calibration, and profiles/attention_traffic.json, keyed by the attention kernel
+    source hash the profiled runs printed."""
+    import csv
+    import glob
+    from collections import defaultdict
+    prof = os.path.join(ROOT, "profiles")
+    w_name = "deepseek_b32_ctx4096"
+    kname = "mla::decode_kernel<4, 64>"
+    shas = {_bench_line(os.path.join(d, "prof_ds.log"))["attention_kernel_source_sha256"]}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        shas.add(_bench_line(os.path.join(d, "pmc", c + ".log"))["attention_kernel_source_sha256"])
+    if len(shas) != 1:
+        raise SystemExit("profiled runs used different attention kernel sources: %s" % shas)
+    sha = shas.pop()
+
+    def short(name):
+        name = name.replace("void ", "", 1)
+        return name.split("(")[0] if not name.startswith("at::") else name.split(")")[0] + ")"
+
+    stats = list(csv.DictReader(open(glob.glob(os.path.join(d, "prof_ds", "*kernel_stats.csv"))[0])))
+    lines = ["# Kernel trace: DeepSeek-shaped decode (h=128, B=32, 4096+1 tokens)", "",
+             "Command (from /tmp with TMPDIR=/tmp; the run includes the bench's clock-settling steps):",
+             "", "    " + TRACE_CMD, "",
+             "Per-step kernels: qprep_kernel (query absorption + RoPE, output zeroing), "
+             "decode_kernel<4,64> (split-K attention), combine_kernel (split merge + W_UV). "
+             "append_kernel, pack_kernel and the fills belong to set-up.", "",
+             "| kernel | calls | average us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        lines.append("| `%s` | %s | %.2f | %.2f | %.2f | %.1f%% |" % (
+            short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    lines += ["", "Attention kernel source sha256 (mla_latent_kv_41_amd/csrc/decode_bf16.hip): `%s`" % sha, ""]
+    open(os.path.join(prof, "decode_step_%s_kernel_trace.md" % w_name), "w").write("\n".join(lines))
+
+    vals = defaultdict(lambda: defaultdict(list))
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        for f in glob.glob(os.path.join(d, "pmc", c, "*counter_collection.csv")):
+            for r in csv.DictReader(open(f)):
+                vals[(short(r["Kernel_Name"]), int(r["Grid_Size"]))][r["Counter_Name"]].append(
+                    float(r["Counter_Value"]))
+    copy = [k for k in vals if "copyBuffer" in k[0] and k[1] == COPY_BYTES // 4096]
+    if len(copy) != 1:
+        raise SystemExit("calibration copy not found in the counter runs")
+    cf = {c: sum(v) / len(v) for c, v in vals[copy[0]].items()}
+    f_fac = COPY_BYTES / (cf["FETCH_SIZE"] * 1024)
+    w_fac = COPY_BYTES / (cf["WRITE_SIZE"] * 1024)
+    dec = [k for k in vals if k[0] == kname]
+    if len(dec) != 1:
+        raise SystemExit("attention kernel not found in the counter runs")
+    dv = {c: sum(v) / len(v) for c, v in vals[dec[0]].items()}
+    fetch_b = dv["FETCH_SIZE"] * 1024 * f_fac
+    write_b = dv["WRITE_SIZE"] * 1024 * w_fac
+    lines = ["# HBM traffic counters: decode_kernel<4,64>, DeepSeek-shaped decode (h=128, B=32, 4096+1 tokens)", "",
+             "Commands (one counter per pass, from /tmp with TMPDIR=/tmp; `--calibrate-copy` adds one 512 MiB "
+             "device-to-device copy, dispatched as `__amd_rocclr_copyBuffer` with grid %d):" % (COPY_BYTES // 4096), ""]
+    lines += ["    " + PMC_CMD.format(c=c) for c in ("FETCH_SIZE", "WRITE_SIZE")]
+    lines += ["", "Summarised with `python3 bench.py --summarize-profiles <out>`.", "",
+              "Attention kernel source sha256 (mla_latent_kv_41_amd/csrc/decode_bf16.hip): `%s`" % sha, "",
+              "| kernel | grid | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB |", "|---|---|---|---|---|"]
+    for (n, g), cs in sorted(vals.items(), key=lambda kv: -sum(kv[1].get("FETCH_SIZE", [0])) / max(1, len(kv[1].get("FETCH_SIZE", [0])))):
+        fs = cs.get("FETCH_SIZE", [float("nan")])
+        ws = cs.get("WRITE_SIZE", [float("nan")])
+        lines.append("| `%s` | %d | %d | %.1f | %.1f |" % (n, g, len(fs), sum(fs) / len(fs), sum(ws) / len(ws)))
+    lines += ["", "Calibration: the 512 MiB copy reads and writes %d bytes; FETCH_SIZE counts %.1f KiB "
+              "(factor %.4f bytes per counted byte) and WRITE_SIZE %.1f KiB (factor %.4f)." % (
+                  COPY_BYTES, cf["FETCH_SIZE"], f_fac, cf["WRITE_SIZE"], w_fac), "",
+              "decode_kernel<4,64> per launch: fetch %.1f MB, write %.1f MB, total %.1f MB." % (
+                  fetch_b / 1e6, write_b / 1e6, (fetch_b + write_b) / 1e6), ""]
+    open(os.path.join(prof, "decode_kernel_%s_hbm_counters.md" % w_name), "w").write("\n".join(lines))
+    rec = {"kernel": "decode_kernel<4,64>", "workload": w_name, "kernel_source_sha256": sha,
+           "fetch_size_kib_per_dispatch": round(dv["FETCH_SIZE"], 1),
+           "write_size_kib_per_dispatch": round(dv["WRITE_SIZE"], 1),
+           "copy_calibration": {"bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+                                "fetch_size_kib": cf["FETCH_SIZE"], "write_size_kib": cf["WRITE_SIZE"],
+                                "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4)},
+           "fetch_bytes_per_launch": int(fetch_b), "write_bytes_per_launch": int(write_b),
+           "bytes_per_launch": int(fetch_b + write_b)}
+    json.dump(rec, open(os.path.join(prof, "attention_traffic.json"), "w"), indent=1)
+    print("summaries written for attention kernel source %s" % sha)
+
 
 def main():
     ap = argparse.ArgumentParser()
@@ -123,7 +225,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 512 MiB device copy first (counter calibration)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write profiles/ summaries from rocprofv3 output under DIR "
+                         "(no GPU work)")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -214,6 +322,7 @@ def main():
         "tokens_per_s": round(tok_s, 1),
         "attention_kernel_ms": round(attn_avg, 5),
         "attention_kernel_samples": len(sampled),
+        "attention_kernel_source_sha256": kernel_source_hash(),
         "roofline": {"bound": "hbm", "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,

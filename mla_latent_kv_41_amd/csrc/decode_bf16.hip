@@ -92,21 +92,20 @@ struct Ic {
 // compiler's wait insertion does not track it (it would otherwise wait for all
 // such loads before unrelated LDS reads); the kernel bounds these loads with
 // explicit vmcnt waits. The offset is formed inside the block (so no per-load
-// offset stays live in a VGPR), M0 (the LDS base) is restored, and the only
-// register written is that temporary. The target buffer is never read while its
-// loads are in flight, so the statement needs no memory clobber; being volatile,
-// it keeps its order against the barriers.
+// offset stays live in a VGPR); M0 takes the LDS base and is declared clobbered
+// (the v_add gives the one wait state between the M0 write and the load). The
+// target buffer is never read while its loads are in flight, so the statement
+// needs no memory clobber; being volatile, it keeps its order against the barriers.
 __device__ __forceinline__ void dma_b128(const u32x4& rsrc, uint32_t lane_off, uint32_t off, uint32_t lds) {
-  uint32_t saved, voff;
+  uint32_t voff;
   asm volatile("" : "+s"(off), "+s"(lds));  // registers, never folded literals
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "v_add_u32 %1, %4, %3\n\t"
-      "buffer_load_dwordx4 %1, %5, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved), "=&v"(voff)
-      : "s"(lds), "v"(lane_off), "s"(off), "s"(rsrc));
+      "s_mov_b32 m0, %1\n\t"
+      "v_add_u32 %0, %3, %2\n\t"
+      "buffer_load_dwordx4 %0, %4, 0 offen lds"
+      : "=&v"(voff)
+      : "s"(lds), "v"(lane_off), "s"(off), "s"(rsrc)
+      : "m0");
 }
 
 // Score MFMA in VGPR form: Sᵀ += A · B with the accumulator in VGPRs. (The
@@ -272,7 +271,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   if (tid == 0) s_restart = 0;
 
   // ---- scores: Sᵀ[32 tokens][32 rows of this wave], SDEPTH fragments in flight
-  constexpr int SDEPTH = 4;
+  constexpr int SDEPTH = 6;
   auto scores = [&](const char* tile, auto hook) __attribute__((always_inline)) {
     f32x16 sc = {};
     u32x4 fa[SDEPTH];
@@ -472,35 +471,23 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     constexpr bool FIRST = decltype(first)::value != 0;
     wait_tiles(i + 1 < n_tiles ? 1 : 0);  // tile i has landed
     lds_barrier();  // tile i and P of tile i - 1 everywhere; tile i - 2 is free
-    const bool more = i + 2 < n_tiles;
-    char* nxt = tile_ptr(Ic<(K + 2) % 4>{});
-    const u32x4 rs = more ? tile_rsrc(i + 2) : u32x4{0u, 0u, 0u, 0u};
-    auto issue_one = [&](int n) __attribute__((always_inline)) {
-      if (more) issue_load(rs, nxt, n);
-    };
-    constexpr int NS = (C::LOADS + 1) / 2;  // loads during the scores (after the first)
-    issue_one(0);
-    f32x16 sc = scores(tile_ptr(kc), [&](int ks) __attribute__((always_inline)) {
-      constexpr int step_ks = C::KS / NS;
+    // tile i + 2 into the buffer of tile i - 2, as one burst ahead of the score
+    // chain: measured cheaper than loads spread through the MFMAs, and far cheaper
+    // than loads among the value phase's transposed LDS reads
+    if (i + 2 < n_tiles) {
+      char* nxt = tile_ptr(Ic<(K + 2) % 4>{});
+      const u32x4 rs = tile_rsrc(i + 2);
 #pragma unroll
-      for (int n = 1; n < NS; ++n)
-        if (ks == n * step_ks - 1) issue_one(n);
-    });
+      for (int n = 0; n < C::LOADS; ++n) issue_load(rs, nxt, n);
+    }
+    f32x16 sc = scores(tile_ptr(kc), [](int) {});
     if (i >= first_masked) apply_mask(sc, i);  // uniform
     SoftState st;
     if constexpr (FIRST) {
 #pragma unroll
       for (int k = 0; k < kSoftSteps; ++k) soft_step(k, sc, st, allow_restart);
-#pragma unroll
-      for (int n = NS; n < C::LOADS; ++n) issue_one(n);
     } else {
-      pv(tile_ptr(Ic<(K + 3) % 4>{}), [&](int f) __attribute__((always_inline)) {
-        constexpr int NV = C::LOADS - NS;  // loads during the values
-        constexpr int NF = 2 * CBW;
-#pragma unroll
-        for (int n = 0; n < NV; ++n)
-          if (f == (n * NF) / NV) issue_one(NS + n);
-      }, [&](int j) __attribute__((always_inline)) {
+      pv(tile_ptr(Ic<(K + 3) % 4>{}), [](int) {}, [&](int j) __attribute__((always_inline)) {
         if (j < kSoftSteps) soft_step(j, sc, st, allow_restart);
       }, Ic<1>{});
     }
