@@ -120,4 +120,54 @@ __device__ __forceinline__ float half_sum(float x) {
 // moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// s_waitcnt that bounds only the vector-memory counter (lgkm and exp left free).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Raw buffer resource over [base, base + bytes): loads at offsets >= bytes return zeros.
+__device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t ba = reinterpret_cast<uint64_t>(base);
+  return u32x4{static_cast<uint32_t>(ba), static_cast<uint32_t>(ba >> 32) & 0xFFFFu, bytes, 0x00020000u};
+}
+constexpr uint32_t kOobOffset = 0xFFFFFFF0u;  // a lane offset past any size bound
+
+// Direct-to-LDS buffer loads: lane l's 16 (or 4) bytes at buffer offset lane_off +
+// off land at LDS address lds + 16 l (4 l). Issued from asm so that the compiler's
+// wait insertion does not track them (it would otherwise wait for all such loads
+// before unrelated LDS reads, and at loop headers); callers bound them with
+// explicit vmcnt waits. The offset is formed inside the block (no per-load offset
+// stays live in a VGPR); M0 takes the LDS base and is declared clobbered (the
+// v_add gives the one wait state between the M0 write and the load). No memory
+// clobber: a buffer being filled is not read before the caller's wait; being
+// volatile, the statement keeps its order against other volatile asm (barriers,
+// waits).
+__device__ __forceinline__ void dma_b128(const u32x4& rsrc, uint32_t lane_off, uint32_t off, uint32_t lds) {
+  uint32_t voff;
+  asm volatile("" : "+s"(off), "+s"(lds));  // registers, never folded literals
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "v_add_u32 %0, %3, %2\n\t"
+      "buffer_load_dwordx4 %0, %4, 0 offen lds"
+      : "=&v"(voff)
+      : "s"(lds), "v"(lane_off), "s"(off), "s"(rsrc)
+      : "m0");
+}
+__device__ __forceinline__ void dma_b32(const u32x4& rsrc, uint32_t lane_off, uint32_t lds) {
+  asm volatile("" : "+s"(lds));
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %1, %2, 0 offen lds"
+      :
+      : "s"(lds), "v"(lane_off), "s"(rsrc)
+      : "m0");
+}
+// LDS address of a __shared__ object, as the 32-bit value M0 takes
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_ptr(p)));
+}
+
 }  // namespace mla

@@ -87,27 +87,6 @@ struct Ic {
   static constexpr int value = V;
 };
 
-// One 16-byte-per-lane direct-to-LDS load: lane l's 16 bytes at buffer offset
-// lane_off + off land at LDS address lds + 16*l. Issued from asm so that the
-// compiler's wait insertion does not track it (it would otherwise wait for all
-// such loads before unrelated LDS reads); the kernel bounds these loads with
-// explicit vmcnt waits. The offset is formed inside the block (so no per-load
-// offset stays live in a VGPR); M0 takes the LDS base and is declared clobbered
-// (the v_add gives the one wait state between the M0 write and the load). The
-// target buffer is never read while its loads are in flight, so the statement
-// needs no memory clobber; being volatile, it keeps its order against the barriers.
-__device__ __forceinline__ void dma_b128(const u32x4& rsrc, uint32_t lane_off, uint32_t off, uint32_t lds) {
-  uint32_t voff;
-  asm volatile("" : "+s"(off), "+s"(lds));  // registers, never folded literals
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "v_add_u32 %0, %3, %2\n\t"
-      "buffer_load_dwordx4 %0, %4, 0 offen lds"
-      : "=&v"(voff)
-      : "s"(lds), "v"(lane_off), "s"(off), "s"(rsrc)
-      : "m0");
-}
-
 // Score MFMA in VGPR form: Sᵀ += A · B with the accumulator in VGPRs. (The
 // compiler selects the AGPR form for every builtin MFMA of this kernel, whose AGPRs
 // hold the value accumulators.) The leading s_nop gives the 2 wait states a VALU
@@ -121,13 +100,6 @@ __device__ __forceinline__ void mfma_v(f32x16& c, const u32x4& a, const u32x4& b
 __device__ __forceinline__ void mfma_v_last(f32x16& c, const u32x4& a, const u32x4& b) {
   asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 4"
       : "+v"(c) : "v"(a), "v"(b));
-}
-
-// s_waitcnt that bounds only the vector-memory counter (lgkm and exp left free).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 }  // namespace
