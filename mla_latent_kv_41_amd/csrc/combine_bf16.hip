@@ -108,74 +108,101 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   // ---- per row (wave w: rows w + 4k): splits holding tokens, M = max_s m_s,
   //      L = Σ_s 2^(m_s - M) l_s, batch 0 weights 2^(m_s - M) l_s / L, lse. Lanes work
   //      in parallel: lane l holds row l's split count, lane sp split sp of each row
-  //      (sp >= 64: a loop), and the eight rows of a wave are reduced together.
+  //      (sp >= 64: a loop); the reductions run on DPP, not through LDS, which the
+  //      partial rows are streaming into.
   int ns_lane = 0;  // lane l < rows: splits holding tokens of row l
   if (l < rows) {
     const int kv = min(s_kv[l], a.max_kv_len);
     ns_lane = kv >= a.n_q ? min((kv + a.chunk - 1) / a.chunk, NS) : 0;
   }
-  int ns_max = ns_lane;
+  const int ns_max = wave_max_i(ns_lane);
+  float lse_v[8];  // lse of row w + 4k (general path) or of this thread's row (lane sp == 0)
+  if (NS <= 8) {  // uniform: thread t takes (row t / 8, split t % 8), one pass
+    const int r = tid >> 3, sp = tid & 7;
+    const bool live = r < rows;
+    int ns = 0;
+    if (live) {
+      const int kv = min(s_kv[r], a.max_kv_len);
+      ns = kv >= a.n_q ? min((kv + a.chunk - 1) / a.chunk, NS) : 0;
+    }
+    f32x2 v = *reinterpret_cast<const f32x2*>(s_ml + (min(r, rows - 1) * NS + min(sp, NS - 1)) * 2);
+    if (sp >= ns) v = f32x2{-INFINITY, 0.f};
+    // reductions over the 8 lanes of the row (quad permutes, then the mirrored half row)
+    float mx = v[0];
+    mx = fmaxf(mx, __int_as_float(dpp_mov<0xB1>(__float_as_int(mx))));
+    mx = fmaxf(mx, __int_as_float(dpp_mov<0x4E>(__float_as_int(mx))));
+    mx = fmaxf(mx, __int_as_float(dpp_mov<0x141>(__float_as_int(mx))));
+    const float mref = mx == -INFINITY ? 0.f : mx;
+    float L = sp < ns ? fast_exp2(v[0] - mref) * v[1] : 0.f;
+    L += __int_as_float(dpp_mov<0xB1>(__float_as_int(L)));
+    L += __int_as_float(dpp_mov<0x4E>(__float_as_int(L)));
+    L += __int_as_float(dpp_mov<0x141>(__float_as_int(L)));
+    const float inv_l = L > 0.f ? 1.f / L : 0.f;
+    lse_v[0] = L > 0.f ? (mx + __log2f(L)) * kLn2 : -INFINITY;
+    if (live && sp < SB) s_w[r * SB + sp] = sp < ns ? fast_exp2(v[0] - mref) * v[1] * inv_l : 0.f;
+    if (live && sp == 0) {
+      s_ns[r] = ns;
+      s_stat[r][0] = mref;
+      s_stat[r][1] = inv_l;
+    }
+  } else {
+    // general: wave w takes rows w + 4k, lane sp split sp (sp >= 64: a loop), the eight
+    // rows of a wave reduced together
+    int nsr[8];
+    float mx[8], L[8];
+    f32x2 v0[8];  // (m, l) of split l of each row
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) ns_max = max(ns_max, __shfl_xor(ns_max, o));
-  ns_max = __builtin_amdgcn_readfirstlane(ns_max);
-  int nsr[8];
-  float mx[8], L[8], lse_v[8];
-  f32x2 v0[8];  // (m, l) of split l of each row
+    for (int k = 0; k < 8; ++k) {
+      const int r = w + 4 * k;
+      nsr[k] = r < rows ? __builtin_amdgcn_readlane(ns_lane, r) : 0;
+      v0[k] = *reinterpret_cast<const f32x2*>(s_ml + (min(r, rows - 1) * NS + min(l, NS - 1)) * 2);
+      if (l >= nsr[k]) v0[k] = f32x2{-INFINITY, 0.f};
+      mx[k] = v0[k][0];
+    }
+    if (NS > 64) {  // uniform
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int r = w + 4 * k;
-    nsr[k] = r < rows ? __builtin_amdgcn_readlane(ns_lane, r) : 0;
-    v0[k] = *reinterpret_cast<const f32x2*>(s_ml + (min(r, rows - 1) * NS + min(l, NS - 1)) * 2);
-    if (l >= nsr[k]) v0[k] = f32x2{-INFINITY, 0.f};
-    mx[k] = v0[k][0];
-  }
-  if (NS > 64) {  // uniform
+      for (int k = 0; k < 8; ++k)
+        for (int sp = l + 64; sp < nsr[k]; sp += 64) mx[k] = fmaxf(mx[k], s_ml[((w + 4 * k) * NS + sp) * 2]);
+    }
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-      for (int sp = l + 64; sp < nsr[k]; sp += 64) mx[k] = fmaxf(mx[k], s_ml[((w + 4 * k) * NS + sp) * 2]);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1)
-#pragma unroll
-    for (int k = 0; k < 8; ++k) mx[k] = fmaxf(mx[k], __shfl_xor(mx[k], o));
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const float mref = mx[k] == -INFINITY ? 0.f : mx[k];
-    L[k] = l < nsr[k] ? fast_exp2(v0[k][0] - mref) * v0[k][1] : 0.f;
-  }
-  if (NS > 64) {  // uniform
+    for (int k = 0; k < 8; ++k) mx[k] = wave_max(mx[k]);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const float mref = mx[k] == -INFINITY ? 0.f : mx[k];
-      for (int sp = l + 64; sp < nsr[k]; sp += 64) {
-        const f32x2 v = *reinterpret_cast<const f32x2*>(s_ml + ((w + 4 * k) * NS + sp) * 2);
-        L[k] += fast_exp2(v[0] - mref) * v[1];
+      L[k] = l < nsr[k] ? fast_exp2(v0[k][0] - mref) * v0[k][1] : 0.f;
+    }
+    if (NS > 64) {  // uniform
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float mref = mx[k] == -INFINITY ? 0.f : mx[k];
+        for (int sp = l + 64; sp < nsr[k]; sp += 64) {
+          const f32x2 v = *reinterpret_cast<const f32x2*>(s_ml + ((w + 4 * k) * NS + sp) * 2);
+          L[k] += fast_exp2(v[0] - mref) * v[1];
+        }
       }
     }
-  }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1)
+    for (int k = 0; k < 8; ++k) L[k] = wave_sum(L[k]);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) L[k] += __shfl_xor(L[k], o);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int r = w + 4 * k;
-    const float mref = mx[k] == -INFINITY ? 0.f : mx[k];
-    const float inv_l = L[k] > 0.f ? 1.f / L[k] : 0.f;
-    lse_v[k] = L[k] > 0.f ? (mx[k] + __log2f(L[k])) * kLn2 : -INFINITY;  // stored at the end
-    if (r >= rows) continue;  // uniform
-    for (int sp = l; sp < SB; sp += 64) {
-      float wgt = 0.f;
-      if (sp < nsr[k]) {
-        const f32x2 v = sp < 64 ? v0[k] : *reinterpret_cast<const f32x2*>(s_ml + (r * NS + sp) * 2);
-        wgt = fast_exp2(v[0] - mref) * v[1] * inv_l;
+    for (int k = 0; k < 8; ++k) {
+      const int r = w + 4 * k;
+      const float mref = mx[k] == -INFINITY ? 0.f : mx[k];
+      const float inv_l = L[k] > 0.f ? 1.f / L[k] : 0.f;
+      lse_v[k] = L[k] > 0.f ? (mx[k] + __log2f(L[k])) * kLn2 : -INFINITY;
+      if (r >= rows) continue;  // uniform
+      for (int sp = l; sp < SB; sp += 64) {
+        float wgt = 0.f;
+        if (sp < nsr[k]) {
+          const f32x2 v = sp < 64 ? v0[k] : *reinterpret_cast<const f32x2*>(s_ml + (r * NS + sp) * 2);
+          wgt = fast_exp2(v[0] - mref) * v[1] * inv_l;
+        }
+        s_w[r * SB + sp] = wgt;
       }
-      s_w[r * SB + sp] = wgt;
-    }
-    if (l == 0) {
-      s_ns[r] = nsr[k];
-      s_stat[r][0] = mref;
-      s_stat[r][1] = inv_l;
+      if (l == 0) {
+        s_ns[r] = nsr[k];
+        s_stat[r][0] = mref;
+        s_stat[r][1] = inv_l;
+      }
     }
   }
 
@@ -300,10 +327,14 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     }
     atomicAdd(a.out + static_cast<int64_t>(m) * width + col, ov);
   }
-  if (kh == 0 && a.lse && l == 0) {
+  if (kh == 0 && a.lse) {
+    if (NS <= 8) {
+      if ((tid & 7) == 0 && (tid >> 3) < rows) a.lse[static_cast<int64_t>(m0 + (tid >> 3)) * a.h + i] = lse_v[0];
+    } else if (l == 0) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (w + 4 * k < rows) a.lse[static_cast<int64_t>(m0 + w + 4 * k) * a.h + i] = lse_v[k];
+      for (int k = 0; k < 8; ++k)
+        if (w + 4 * k < rows) a.lse[static_cast<int64_t>(m0 + w + 4 * k) * a.h + i] = lse_v[k];
+    }
   }
 }
 

@@ -113,6 +113,41 @@ __device__ __forceinline__ float half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Wave-wide reductions without the LDS crossbar (which __shfl uses): butterflies
+// inside each 16-lane row by DPP (lanes at distance 1 and 2 by quad permutes, then
+// the mirrored half rows and the mirrored rows), then the four row results read
+// with v_readlane and combined in a fixed order. The result is wave-uniform.
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov(int x) {
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, false);
+}
+template <typename Op>
+__device__ __forceinline__ float wave_reduce_f(float x, Op op) {
+  x = op(x, __int_as_float(dpp_mov<0xB1>(__float_as_int(x))));   // quad_perm [1,0,3,2]
+  x = op(x, __int_as_float(dpp_mov<0x4E>(__float_as_int(x))));   // quad_perm [2,3,0,1]
+  x = op(x, __int_as_float(dpp_mov<0x141>(__float_as_int(x))));  // row_half_mirror
+  x = op(x, __int_as_float(dpp_mov<0x140>(__float_as_int(x))));  // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return op(op(r0, r1), op(r2, r3));
+}
+__device__ __forceinline__ float wave_max(float x) {
+  return wave_reduce_f(x, [](float p, float q) { return fmaxf(p, q); });
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  return wave_reduce_f(x, [](float p, float q) { return p + q; });
+}
+__device__ __forceinline__ int wave_max_i(int x) {
+  x = max(x, dpp_mov<0xB1>(x));
+  x = max(x, dpp_mov<0x4E>(x));
+  x = max(x, dpp_mov<0x141>(x));
+  x = max(x, dpp_mov<0x140>(x));
+  return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+
 // Workgroup barrier for LDS traffic between waves: this wave's LDS reads and
 // writes are complete before it arrives (lgkmcnt(0) in the same block), but its
 // global loads, direct-to-LDS loads included, stay in flight; callers wait for
