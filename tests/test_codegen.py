@@ -1,0 +1,65 @@
+"""Properties of the gfx950 code the kernels compile to (CPU only: hipcc emits the
+device assembly without a GPU).
+
+- M0 is written only by the direct-to-LDS load sequences, which declare it
+  clobbered; that is sound only while no compiler-generated instruction reads M0,
+  so the instructions that read it implicitly must be absent, apart from those loads.
+- No scalar-cache writes (scalar stores, scalar atomics, write-back of that cache).
+- No packed fp32 VALU instructions (the build disables their formation).
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from mla_latent_kv_41_amd import build
+
+HIPCC = build.HIPCC
+
+
+def device_asm(src):
+    flags = [f for f in build.FLAGS if f not in ("-fPIC", "-shared")]
+    res = subprocess.run([HIPCC, *flags, "--cuda-device-only", "-S", src, "-o", "-"],
+                         capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    return res.stdout
+
+
+def instructions(asm):
+    for line in asm.splitlines():
+        s = line.strip()
+        if not s or s.startswith((";", ".", "_")) or s.endswith(":"):
+            continue
+        yield s.split(";")[0].strip()
+
+
+# instructions that read M0 implicitly (LDS-direct and interpolation forms, GWS,
+# messages, relative register moves, LDS "add TID" forms)
+IMPLICIT_M0 = re.compile(r"^(s_sendmsg|s_movrel|v_movrel|v_interp|ds_gws|ds_\w*addtid|lds_direct|"
+                         r"s_ttracedata)")
+SCALAR_WRITE = re.compile(r"^(s_store|s_scratch_store|s_buffer_store|s_atomic|s_buffer_atomic|"
+                          r"s_dcache_wb|s_dcache_discard)")
+PACKED_F32 = re.compile(r"^v_pk_(add|mul|fma)_f32")
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipcc") is None, reason="hipcc not found")
+@pytest.mark.parametrize("name", ["decode_bf16", "combine_bf16", "prep_bf16", "append", "f32_path"])
+def test_device_code_properties(name):
+    asm = device_asm(os.path.join(build.CSRC, name + ".hip"))
+    insts = list(instructions(asm))
+    assert insts, "no instructions parsed"
+    for k, s in enumerate(insts):
+        mnem = s.split()[0]
+        assert not IMPLICIT_M0.match(mnem), s
+        assert not SCALAR_WRITE.match(mnem), s
+        assert not PACKED_F32.match(mnem), s
+        if re.search(r"\bm0\b", s):
+            # only writes of M0 from an SGPR, each followed by a direct-to-LDS load
+            assert re.match(r"^s_mov_b32 m0, s\d+$", s), s
+            nxt = [t for t in insts[k + 1:k + 4] if t.startswith("buffer_load")]
+            assert nxt and nxt[0].endswith(" lds"), (s, insts[k + 1:k + 4])
+        if mnem.startswith("buffer_load") and s.endswith(" lds"):
+            prev = [t for t in insts[max(0, k - 3):k] if "m0" in t]
+            assert prev, ("direct-to-LDS load without its M0 write", s)
