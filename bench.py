@@ -73,7 +73,32 @@ def algorithmic(w):
     cache_bytes = float(kv.sum()) * (w.d_c + w.d_r) * 2
     weight_bytes = 2.0 * w.d_c * w.h * (w.d_n + w.d_v)
     io_bytes = M * w.h * (w.d_n + w.d_r) * 2 + M * w.h * w.d_v * 4
+    if w.gated:  # the output gate's logits x · W_G, x [M, d_model] bf16, W_G [d_model, h*d_v] bf16
+        flops += 2.0 * M * w.d_model * w.h * w.d_v
+        weight_bytes += 2.0 * w.d_model * w.h * w.d_v
+        io_bytes += 2.0 * M * w.d_model
     return flops, cache_bytes, cache_bytes + weight_bytes + io_bytes
+
+
+def attention_flops(w):
+    """FLOPs of the attention kernel alone: scores and the value sum over the
+    visible tokens."""
+    vis = sum(float(n) - w.n_q + j + 1 for n in w.kv_lens for j in range(w.n_q))
+    return 2.0 * w.h * vis * (w.d_c + w.d_r) + 2.0 * w.h * vis * w.d_c
+
+
+def config_desc(w):
+    import numpy as np
+    d = {"workload": w.name, "heads": w.h, "batch": w.batch, "query_tokens": w.n_q,
+         "kv_len_max": int(w.kv_max), "kv_len_total": int(np.sum(w.kv_lens)), "d_c": w.d_c,
+         "d_rope": w.d_r, "d_qk_nope": w.d_n, "d_v": w.d_v, "layer_copies_rotated": COPIES}
+    if w.paged:
+        d["cache"] = "paged bf16, %d-token blocks, pool %d blocks" % (w.block_size, w.pool_blocks)
+    else:
+        d["cache"] = "contiguous bf16 [%d, %d, %d]" % (w.batch, w.kv_max, w.row)
+    if w.gated:
+        d["gate_d_model"] = w.d_model
+    return d
 
 
 def kernel_source_hash():
@@ -225,6 +250,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 512 MiB device copy first (counter calibration)")
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5],
+                    help="workload: 2 DeepSeek-shaped (default, the headline), 3 paged long "
+                         "context, 4 ragged with two queries, 5 gated h=64 without RoPE")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write profiles/ summaries from rocprofv3 output under DIR "
                          "(no GPU work)")
@@ -242,7 +270,7 @@ def main():
     from mla_latent_kv_41_amd import mla, synth
     from mla_latent_kv_41_amd.harness import GpuStep
 
-    w = synth.make_workload(2)
+    w = synth.make_workload(args.config)
     t = synth.draw(w)
     log("workload %s: B=%d kv_len=%d h=%d row=%d" % (w.name, w.batch, w.kv_max, w.h, w.row))
     steps = [GpuStep(w, t, poison=False) for _ in range(COPIES)]
@@ -296,9 +324,25 @@ def main():
     cache_gbps = cache_bytes / (ms * 1e-3) / 1e9
     tok_s = w.batch * w.n_q / (ms * 1e-3)
     attn_gbps = cache_bytes / (attn_avg * 1e-3) / 1e9
-    traffic = traffic_from_profile(1)
+    traffic = traffic_from_profile(1) if args.config == 2 else None
+    attn_flops = attention_flops(w)
+    attn_tflops = attn_flops / (attn_avg * 1e-3) / 1e12
+    mfma_bound = args.config == 4  # 256 score rows per tile: the matrix cores bind
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": round(attn_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic, "hbm_GBps": round(attn_gbps, 1),
+                "hbm_frac": round(attn_gbps / HBM_PEAK_GBPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "mfma_TFLOPs": round(attn_tflops, 1),
+                "mfma_frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+    roof.update({"kernel": "decode_kernel (split-K attention over the latent cache)",
+                 "algorithmic_bytes_per_launch": cache_bytes, "algorithmic_flops_per_launch": attn_flops})
     out = {
         "metric": "MLA decode TFLOP/s + latent-cache GB/s (% roofline), h=128 B=32 ctx=4096",
+        # other workloads (--config) report the same quantities for their own shapes
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -310,10 +354,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; N(0,1) RMS-normalised latents, N(0,1/512) weights)",
-        "config": {"workload": w.name, "heads": w.h, "batch": w.batch, "cached_tokens": 4096,
-                   "kv_len": w.kv_max, "d_c": w.d_c, "d_rope": w.d_r, "d_qk_nope": w.d_n,
-                   "d_v": w.d_v, "cache": "contiguous bf16 [32, 4097, 576]",
-                   "layer_copies_rotated": COPIES},
+        "config": config_desc(w),
         "latent_cache_GBps": round(cache_gbps, 1),
         "latent_cache_frac_of_hbm_peak": round(cache_gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_GBps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
@@ -323,14 +364,9 @@ def main():
         "attention_kernel_ms": round(attn_avg, 5),
         "attention_kernel_samples": len(sampled),
         "attention_kernel_source_sha256": kernel_source_hash(),
-        "roofline": {"bound": "hbm", "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic,
-                     "kernel": "decode_kernel<4,64> (split-K attention over the latent cache)",
-                     "algorithmic_bytes_per_launch": cache_bytes,
-                     "mfma_TFLOPs": round(flops * 0.9714 / (attn_avg * 1e-3) / 1e12, 1)},
+        "roofline": roof,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.config == 2:
         out["cpu_baseline"] = cpu_baseline(w, t)
     print(json.dumps(out), flush=True)
 

@@ -65,8 +65,8 @@ Plan plan_bf16(const Resolved& r, const mla_decode_args* a) {
   const int rows = r.h * a->n_q;
   p.nw = rows % 128 == 0 ? 4 : 2;
   p.hgroups = rows / (32 * p.nw);
-  const int wg_per_cu = 4 / p.nw;  // one wave per SIMD
-  const int64_t target = 256LL * wg_per_cu;
+  // one workgroup per CU either way: four tile buffers take most of the LDS
+  const int64_t target = 256;
   const int L = a->max_kv_len;
   const int64_t units = static_cast<int64_t>(a->batch) * p.hgroups;
   // one workgroup per slot when every sequence is as long as the longest

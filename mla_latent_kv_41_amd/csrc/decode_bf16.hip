@@ -68,7 +68,7 @@ __device__ __forceinline__ int swz(int t) {
 
 template <int NW, int DR>
 struct Cfg {
-  static constexpr int NBUF = NW == 4 ? 4 : 2;             // tile buffers
+  static constexpr int NBUF = 4;                           // tile buffers
   static constexpr int ROW = 512 + DR;                     // elements per cache row
   static constexpr int ROWB = ROW * 2;                     // bytes per cache row
   static constexpr int CH = ROW / 8;                       // 16-byte chunks per row
@@ -112,8 +112,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // direct-to-LDS loads landing in another, so they need no load wait.
   __shared__ __attribute__((aligned(1024))) char s_tile0[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char s_tile1[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char s_tile2[NBUF > 2 ? C::TILE_BYTES : 16];
-  __shared__ __attribute__((aligned(1024))) char s_tile3[NBUF > 3 ? C::TILE_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char s_tile2[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char s_tile3[C::TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char s_p[RB * 2 * 1024];  // P fragments [row block][k-step][lane]
   __shared__ float s_inv[C::R];                                      // 1 / l per row (epilogue)
   __shared__ int s_restart;
@@ -317,13 +317,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       l_run += half_sum((st.ps[0] + st.ps[1]) + (st.ps[2] + st.ps[3]));
     }
   };
-  auto softmax = [&](bool masked, f32x16 sc, int it, bool allow_restart) __attribute__((always_inline)) {
-    if (masked) apply_mask(sc, it);  // uniform
-    SoftState st;
-#pragma unroll
-    for (int k = 0; k < kSoftSteps; ++k) soft_step(k, sc, st, allow_restart);
-    return st.r;
-  };
 
   // ---- values for this wave's CBW column blocks and every row block:
   //      Oᵀ[c][r] += Σ_t Cᵀ[c][t] · Pᵀ[t][r]; P of all rows comes from LDS one
@@ -373,14 +366,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     else return s_tile3;
   };
 
-  // P of this wave's rows to LDS (B-operand order of the value MFMA) and the
-  // restart request of the tile
-  auto publish = [&](const Soft& cur) __attribute__((always_inline)) {
-    *(lds_u32x4*)(lds_ptr(s_p) + (w * 2 + 0) * 1024 + l * 16) = cur.p[0];
-    *(lds_u32x4*)(lds_ptr(s_p) + (w * 2 + 1) * 1024 + l * 16) = cur.p[1];
-    if (__builtin_amdgcn_ballot_w64(cur.overrun) && l == 0) s_restart = 1;
-  };
-
   // Tiles from `first_masked` on hold tokens some row must not see (past the end of
   // the range, or past a row's causal limit); the tiles before it need no mask.
   const int bound = min(t_end - 1, kv - a.n_q);
@@ -391,45 +376,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     if (ahead >= 2) wait_vm<2 * C::LOADS>();
     else if (ahead == 1) wait_vm<C::LOADS>();
     else wait_vm<0>();
-  };
-
-  // Step i: scores, softmax and values of tile i (buffer i % NBUF); tiles up to
-  // i + NBUF - 2 were issued before, tile i + NBUF - 1 goes into the buffer of tile
-  // i - 1. Returns true when some row asked for a restart at tile i.
-  auto step = [&](auto kc, int i, bool allow_restart) __attribute__((always_inline)) -> bool {
-    constexpr int K = decltype(kc)::value;
-    if constexpr (NBUF == 4) wait_tiles(min(n_tiles - 1, i + 2) - i);
-    else wait_vm<0>();
-    lds_barrier();  // tile i everywhere; every wave is done with tile i - 1 and P
-    // The loads of tile i + NBUF - 1 go out one at a time, spread over the step: a
-    // CU keeps only about one tile of loads in flight, and a load issued while that
-    // capacity is taken stalls this wave until an earlier one drains.
-    const bool more = i + NBUF - 1 < n_tiles;
-    char* nxt = tile_ptr(Ic<(K + NBUF - 1) % NBUF>{});
-    const u32x4 rs = more ? tile_rsrc(i + NBUF - 1) : u32x4{0u, 0u, 0u, 0u};
-    auto issue_one = [&](int n) __attribute__((always_inline)) {
-      if (more) issue_load(rs, nxt, n);
-    };
-    // load n goes out after score k-step kS(n) or value fragment kV(n)
-    constexpr int NS = (C::LOADS + 1) / 2;  // loads during the scores (after the first)
-    issue_one(0);
-    const f32x16 sc = scores(tile_ptr(kc), [&](int ks) __attribute__((always_inline)) {
-      constexpr int step_ks = C::KS / NS;
-#pragma unroll
-      for (int n = 1; n < NS; ++n)
-        if (ks == n * step_ks - 1) issue_one(n);
-    });
-    publish(softmax(i >= first_masked, sc, i, allow_restart));
-    lds_barrier();  // P of every row
-    const int restart = s_restart;
-    pv(tile_ptr(kc), [&](int f) __attribute__((always_inline)) {
-      constexpr int NV = C::LOADS - NS;  // loads during the values
-      constexpr int NF = 2 * CBW;
-#pragma unroll
-      for (int n = 0; n < NV; ++n)
-        if (f == (n * NF) / NV) issue_one(NS + n);
-    }, [](int) {}, Ic<0>{});
-    return restart != 0;
   };
 
   // Four tile buffers, pipelined on the value side. Step i computes tile i's scores,
@@ -474,7 +420,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 
   auto prologue = [&]() __attribute__((always_inline)) {
     if (paged) pg_next = page_id(0);
-    constexpr int AHEAD = NBUF == 4 ? 2 : 1;  // tiles issued before the first step
+    constexpr int AHEAD = 2;  // tiles issued before the first step
 #pragma unroll
     for (int k = 0; k < AHEAD; ++k)
       if (k < n_tiles) issue_tile(k, k == 0 ? s_tile0 : s_tile1);
@@ -500,7 +446,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     l_run = 0.f;
     if (pass > 0) prologue();
     bool restart = false;
-    if constexpr (NBUF == 4) {
+    {
       restart = vstep(Ic<0>{}, Ic<1>{}, 0, allow_restart);
       for (int i = 1; i < n_tiles && !restart; i += 4) {
 #define MLA_VSTEP(KK, D) \
@@ -518,11 +464,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         const int kl = (n_tiles - 1) & 3;
         const char* lt = kl == 0 ? s_tile0 : kl == 1 ? s_tile1 : kl == 2 ? s_tile2 : s_tile3;
         pv(lt, [](int) {}, [](int) {}, Ic<0>{});
-      }
-    } else {
-      for (int i = 0; i < n_tiles && !restart; i += 2) {
-        restart = step(Ic<0>{}, i, allow_restart);
-        if (!restart && i + 1 < n_tiles) restart = step(Ic<1>{}, i + 1, allow_restart);
       }
     }
     wait_vm<0>();  // this wave's loads have landed (a restart leaves some in flight)
