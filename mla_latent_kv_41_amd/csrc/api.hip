@@ -148,7 +148,7 @@ mla_status check_decode(const Resolved& r, const mla_decode_args* a) {
     const int R = rows % 128 == 0 ? 128 : 64;
     if (R % a->n_q != 0 || r.h % (R / a->n_q) != 0) return MLA_E_UNSUPPORTED;
     if (R == 64 && r.d_r != 0) return MLA_E_UNSUPPORTED;  // 64-row workgroups are position-free only
-    if (a->gate_x && (a->d_model % kGateSplit != 0 || (r.h * 128) % 512 != 0)) return MLA_E_UNSUPPORTED;
+    if (a->gate_x && (a->d_model % (kGateSplit * 16) != 0 || (r.h * 128) % 128 != 0)) return MLA_E_UNSUPPORTED;
   }
   return MLA_OK;
 }
