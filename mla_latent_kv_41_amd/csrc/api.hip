@@ -58,6 +58,7 @@ struct Plan {
   int chunk;     // tokens per range, a multiple of kTile
   int comb_rows;    // combine: query rows per workgroup (<= 32)
   int comb_splits;  // combine: partial half rows staged per row and batch
+  int comb_slots;   // combine: staged half rows per batch (256, or 128 with two workgroups per CU)
 };
 
 Plan plan_bf16(const Resolved& r, const mla_decode_args* a) {
@@ -90,10 +91,13 @@ Plan plan_bf16(const Resolved& r, const mla_decode_args* a) {
   p.n_splits = static_cast<int>((L + chunk - 1) / chunk);
   // combine grid: (h, 2 latent halves, M / rows); halve the rows until the grid fills
   // the CUs; splits staged per batch fill the 256 half-row slots
+  // with 64 or more query rows, 16-row workgroups that stage 128 half rows, two per CU
+  // (one stages while the other computes); else up to 32 rows and 256 half rows
   const int M = a->batch * a->n_q;
-  p.comb_rows = std::min(32, M);
+  p.comb_slots = M >= 64 ? 128 : 256;
+  p.comb_rows = std::min(p.comb_slots == 128 ? 16 : 32, M);
   while (p.comb_rows > 1 && 2LL * r.h * ((M + p.comb_rows - 1) / p.comb_rows) < 256) p.comb_rows = (p.comb_rows + 1) / 2;
-  p.comb_splits = std::min(p.n_splits, 256 / p.comb_rows);
+  p.comb_splits = std::min(p.n_splits, p.comb_slots / p.comb_rows);
   return p;
 }
 
@@ -264,6 +268,7 @@ mla_status decode_impl(const mla_dims* dims, const CacheRef& cache, const mla_de
   c.max_kv_len = a->max_kv_len;
   c.rows_per_wg = p.comb_rows;
   c.splits_per_batch = p.comb_splits;
+  c.slots = p.comb_slots;
   return launch_combine_bf16(c, stream) == hipSuccess ? MLA_OK : MLA_E_HIP;
 }
 

@@ -18,10 +18,15 @@ namespace {
 constexpr int kGateSplit = 16;          // K-splits of the gate GEMM
 constexpr int kHalf = 256;              // latent columns per workgroup (half of d_c)
 constexpr int kSlotBytes = kHalf * 2;   // one staged half partial row (bf16)
-constexpr int kSlots = 256;             // staged half rows per batch (128 KiB)
 constexpr int kAStride = kHalf * 2 + 16;  // bytes per o_lat half row in LDS (padded)
-constexpr int kMlCap = 3072;            // (m, l) pairs of a workgroup staged in LDS
-constexpr int kStageLoads = kSlots / 2 / 4;  // partial-row loads per wave and batch
+// SLOTS staged half rows per batch: 256 (128 KiB, one workgroup per CU) or 128 (two
+// workgroups per CU, for many row blocks: one stages while the other computes)
+template <int SLOTS>
+struct CombCfg {
+  static constexpr int kSlots = SLOTS;
+  static constexpr int kMlCap = SLOTS == 256 ? 3072 : 1024;  // (m, l) pairs staged in LDS
+  static constexpr int kStageLoads = SLOTS / 2 / 4;          // partial-row loads per wave and batch
+};
 }  // namespace
 
 // grid (h, 2, ceil(M / rows_per_wg)), 256 threads. Workgroup (i, kh, mb) takes head i,
@@ -40,7 +45,11 @@ constexpr int kStageLoads = kSlots / 2 / 4;  // partial-row loads per wave and b
 // the statistics are done, and the merge waits for the partial rows only. Partial
 // rows of splits past a sequence's end are staged too (the merge skips them), so
 // every wave issues a fixed number of loads; slots past the rows read zeros.
+template <int SLOTS>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  using CC = CombCfg<SLOTS>;
+  constexpr int kSlots = CC::kSlots, kMlCap = CC::kMlCap, kStageLoads = CC::kStageLoads;
+  static_assert(32 * kAStride * 2 <= kSlots * kSlotBytes, "o_lat staging fits the slots");
   __shared__ __attribute__((aligned(1024))) char s_part[kSlots * kSlotBytes];
   __shared__ __attribute__((aligned(16))) float s_ml[kMlCap * 2];  // (m, l) of (row, split)
   __shared__ float s_w[kSlots];     // weight of each staged half row
@@ -340,13 +349,21 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 
 hipError_t launch_combine_bf16(const CombineArgs& a, hipStream_t s) {
   const int M = a.batch * a.n_q;
-  if (a.rows_per_wg < 1 || a.rows_per_wg > 32 || a.rows_per_wg * a.splits_per_batch > kSlots ||
-      a.rows_per_wg * a.n_splits > kMlCap)
+  const bool half = a.rows_per_wg <= 16 && a.rows_per_wg * a.splits_per_batch <= CombCfg<128>::kSlots &&
+                    a.rows_per_wg * a.n_splits <= CombCfg<128>::kMlCap && a.slots == 128;
+  const int slots = half ? CombCfg<128>::kSlots : CombCfg<256>::kSlots;
+  const int ml_cap = half ? CombCfg<128>::kMlCap : CombCfg<256>::kMlCap;
+  if (a.rows_per_wg < 1 || a.rows_per_wg > 32 || a.rows_per_wg * a.splits_per_batch > slots ||
+      a.rows_per_wg * a.n_splits > ml_cap)
     return hipErrorInvalidValue;
   // buffer offsets are 32-bit
   if (static_cast<int64_t>(a.batch) * a.n_splits * a.n_q * a.h * 512 * 2 >= (int64_t(1) << 32) - 16)
     return hipErrorInvalidValue;
-  combine_kernel<<<dim3(a.h, 2, (M + a.rows_per_wg - 1) / a.rows_per_wg), 256, 0, s>>>(a);
+  const dim3 grid(a.h, 2, (M + a.rows_per_wg - 1) / a.rows_per_wg);
+  if (half)
+    combine_kernel<128><<<grid, 256, 0, s>>>(a);
+  else
+    combine_kernel<256><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -57,7 +57,8 @@ struct CombineArgs {
   float* lse;               // [M][h] or nullptr
   int32_t batch, n_q, h, n_splits, chunk, max_kv_len;
   int32_t rows_per_wg;       // query rows per workgroup, 1..32
-  int32_t splits_per_batch;  // half partial rows staged per row and batch (rows * splits <= 256)
+  int32_t splits_per_batch;  // half partial rows staged per row and batch (rows * splits <= slots)
+  int32_t slots;             // staged half rows per batch: 256, or 128 (two workgroups per CU)
 };
 hipError_t launch_combine_bf16(const CombineArgs& a, hipStream_t s);
 
