@@ -101,9 +101,14 @@ def config_desc(w):
     return d
 
 
+KERNEL_SOURCES = ("decode_bf16.hip", "common.hpp")  # the attention kernel and its device helpers
+
+
 def kernel_source_hash():
-    p = os.path.join(ROOT, "mla_latent_kv_41_amd", "csrc", "decode_bf16.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, "mla_latent_kv_41_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
 
 
 def traffic_from_profile(per_launch_units):
@@ -192,7 +197,7 @@ def summarize_profiles(d):
         lines.append("| `%s` | %s | %.2f | %.2f | %.2f | %.1f%% |" % (
             short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
-    lines += ["", "Attention kernel source sha256 (mla_latent_kv_41_amd/csrc/decode_bf16.hip): `%s`" % sha, ""]
+    lines += ["", "Attention kernel source sha256 (mla_latent_kv_41_amd/csrc/decode_bf16.hip + common.hpp): `%s`" % sha, ""]
     open(os.path.join(prof, "decode_step_%s_kernel_trace.md" % w_name), "w").write("\n".join(lines))
 
     vals = defaultdict(lambda: defaultdict(list))
@@ -218,7 +223,7 @@ def summarize_profiles(d):
              "device-to-device copy, dispatched as `__amd_rocclr_copyBuffer` with grid %d):" % (COPY_BYTES // 4096), ""]
     lines += ["    " + PMC_CMD.format(c=c) for c in ("FETCH_SIZE", "WRITE_SIZE")]
     lines += ["", "Summarised with `python3 bench.py --summarize-profiles <out>`.", "",
-              "Attention kernel source sha256 (mla_latent_kv_41_amd/csrc/decode_bf16.hip): `%s`" % sha, "",
+              "Attention kernel source sha256 (mla_latent_kv_41_amd/csrc/decode_bf16.hip + common.hpp): `%s`" % sha, "",
               "| kernel | grid | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB |", "|---|---|---|---|---|"]
     for (n, g), cs in sorted(vals.items(), key=lambda kv: -sum(kv[1].get("FETCH_SIZE", [0])) / max(1, len(kv[1].get("FETCH_SIZE", [0])))):
         fs = cs.get("FETCH_SIZE", [float("nan")])
@@ -231,6 +236,7 @@ def summarize_profiles(d):
                   fetch_b / 1e6, write_b / 1e6, (fetch_b + write_b) / 1e6), ""]
     open(os.path.join(prof, "decode_kernel_%s_hbm_counters.md" % w_name), "w").write("\n".join(lines))
     rec = {"kernel": "decode_kernel<4,64>", "workload": w_name, "kernel_source_sha256": sha,
+           "kernel_sources": ["mla_latent_kv_41_amd/csrc/" + f for f in KERNEL_SOURCES],
            "fetch_size_kib_per_dispatch": round(dv["FETCH_SIZE"], 1),
            "write_size_kib_per_dispatch": round(dv["WRITE_SIZE"], 1),
            "copy_calibration": {"bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
