@@ -278,6 +278,26 @@ def test_large_score_jump_restarts_the_range():
     check_bf16(out, ref, what="all heads after a score jump")
 
 
+@pytest.mark.parametrize("batch,d_model", [(40, 8192), (3, 2048)])
+def test_gate_row_blocks_and_widths(batch, d_model):
+    """The gate GEMM over more than one 32-row block of queries, with K splits of 512
+    rows (two staged chunks) or 128 rows (one partial chunk)."""
+    w = synth.make_workload(5, batch=batch, ctx=100)
+    w.d_model = d_model
+    t = synth.draw(w)
+    say("gated case B=%d d_model=%d" % (batch, d_model))
+    out = GpuStep(w, t).decode().cpu().numpy().astype(np.float64)
+    ref = oracle_out(w, t)
+    # 101 visible tokens do not average bf16 rounding out: each output is held to the
+    # first-order bound of the ungated path (the gate scales an output by σ(g) < 1, and
+    # its logits are exact bf16 products summed in fp32)
+    bound = bf16_error_bound(w, t)
+    err = np.abs(out - ref)
+    say("  max err/bound %.3f, max-abs/rms %.4f" % (float(np.max(err / bound)), err.max() / np.sqrt(np.mean(ref ** 2))))
+    assert np.all(np.isfinite(out))
+    assert np.max(err / bound) <= 1.0
+
+
 # ------------------------------------------------------------------ bf16: full sizes, sampled
 
 FULL = {
