@@ -91,10 +91,11 @@ Plan plan_bf16(const Resolved& r, const mla_decode_args* a) {
   p.n_splits = static_cast<int>((L + chunk - 1) / chunk);
   // combine grid: (h, 2 latent halves, M / rows); halve the rows until the grid fills
   // the CUs; splits staged per batch fill the 256 half-row slots
-  // with 64 or more query rows, 16-row workgroups that stage 128 half rows, two per CU
-  // (one stages while the other computes); else up to 32 rows and 256 half rows
+  // with 16 or more query rows, workgroups of up to 16 rows that stage 128 half rows,
+  // two per CU (one stages while the other computes: measured faster at every such
+  // shape); else up to 32 rows and 256 half rows, so few rows take many splits at once
   const int M = a->batch * a->n_q;
-  p.comb_slots = M >= 64 ? 128 : 256;
+  p.comb_slots = M >= 16 ? 128 : 256;
   p.comb_rows = std::min(p.comb_slots == 128 ? 16 : 32, M);
   while (p.comb_rows > 1 && 2LL * r.h * ((M + p.comb_rows - 1) / p.comb_rows) < 256) p.comb_rows = (p.comb_rows + 1) / 2;
   p.comb_splits = std::min(p.n_splits, p.comb_slots / p.comb_rows);
