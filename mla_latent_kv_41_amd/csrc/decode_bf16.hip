@@ -114,9 +114,13 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) char s_tile1[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char s_tile2[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char s_tile3[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char s_p[RB * 2 * 1024];  // P fragments [row block][k-step][lane]
-  __shared__ float s_inv[C::R];                                      // 1 / l per row (epilogue)
-  __shared__ int s_restart;
+  // P fragments [parity][row block][k-step][lane]: P of tile i goes into buffer i % 2,
+  // so publishing it never waits for readers of tile i - 1's P. After the last step's
+  // barrier, the buffer the last tile did not use holds 1 / l per row.
+  constexpr int PBUF = RB * 2 * 1024;
+  __shared__ __attribute__((aligned(16))) char s_p[2 * PBUF];
+  static_assert(4 * C::TILE_BYTES + 2 * PBUF <= 160 * 1024, "LDS");
+  static_assert(16 + 4 * C::R <= PBUF, "1 / l fits a P buffer");
 
   const int tid = threadIdx.x, l = tid % 64;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64);  // wave index, uniform
@@ -240,7 +244,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   float m_ref = -INFINITY;   // this row's fixed reference max
   float m_seen = -INFINITY;  // largest score this row has seen
   float l_run = 0.f;
-  if (tid == 0) s_restart = 0;
 
   // ---- scores: Sᵀ[32 tokens][32 rows of this wave], SDEPTH fragments in flight
   constexpr int SDEPTH = 6;
@@ -324,7 +327,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   //      four-deep window
   // `mstep(j)` runs after value MFMA j (of 2*CBW*RB); with `pinned`, each MFMA and
   // its mstep stay together in issue order (VALU work issued while the MFMA runs)
-  auto pv = [&](const char* tile, auto hook, auto mstep, auto pinned) __attribute__((always_inline)) {
+  auto pv = [&](const char* tile, const char* pbuf, auto hook, auto mstep, auto pinned) __attribute__((always_inline)) {
     auto load = [&](int f) __attribute__((always_inline)) {
       const int kk = f / CBW, cb = CBW * w + f % CBW;
       lds_char* tb = lds_ptr(tile) + kk * 16 * 128 + (cb >> 1) * 4096;
@@ -344,7 +347,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       const int kk = f / CBW, cbl = f % CBW;
       if (cbl == 0) {
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) pb[rb] = *(lds_u32x4*)(lds_ptr(s_p) + (rb * 2 + kk) * 1024 + l * 16);
+        for (int rb = 0; rb < RB; ++rb) pb[rb] = *(lds_u32x4*)(lds_ptr(pbuf) + (rb * 2 + kk) * 1024 + l * 16);
       }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
@@ -380,11 +383,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 
   // Four tile buffers, pipelined on the value side. Step i computes tile i's scores,
   // then runs tile i's softmax interleaved with the value MFMAs of tile i - 1 (whose P
-  // was published at the end of step i - 1), and publishes P of tile i after every
-  // wave is done with P of tile i - 1. Tiles i and i - 1 are in use, tile i + 1 is in
-  // flight, and tile i + 2 goes into the buffer of tile i - 2. `first` is step 0,
-  // which has no previous tile. Returns true when some row asked for a restart.
-  auto vstep = [&](auto kc, auto first, int i, bool allow_restart) __attribute__((always_inline)) -> bool {
+  // was published at the end of step i - 1), and publishes P of tile i into the other
+  // P buffer. One barrier per step: tiles i and i - 1 are in use, tile i + 1 is in
+  // flight, tile i + 2 goes into the buffer of tile i - 2, and P of tile i - 2 (the
+  // buffer P of tile i overwrites) was last read in step i - 1. `first` is step 0,
+  // which has no previous tile. A score past the headroom only marks the wave's
+  // `ovr`; the range is restarted after it (the flags are exchanged once there).
+  uint64_t ovr = 0;
+  auto vstep = [&](auto kc, auto first, int i, bool allow_restart) __attribute__((always_inline)) {
     constexpr int K = decltype(kc)::value;
     constexpr bool FIRST = decltype(first)::value != 0;
     wait_tiles(i + 1 < n_tiles ? 1 : 0);  // tile i has landed
@@ -405,16 +411,13 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int k = 0; k < kSoftSteps; ++k) soft_step(k, sc, st, allow_restart);
     } else {
-      pv(tile_ptr(Ic<(K + 3) % 4>{}), [](int) {}, [&](int j) __attribute__((always_inline)) {
+      pv(tile_ptr(Ic<(K + 3) % 4>{}), s_p + ((K + 1) & 1) * PBUF, [](int) {}, [&](int j) __attribute__((always_inline)) {
         if (j < kSoftSteps) soft_step(j, sc, st, allow_restart);
       }, Ic<1>{});
     }
-    if (__builtin_amdgcn_ballot_w64(st.r.overrun) && l == 0) s_restart = 1;
-    lds_barrier();  // every wave is done with P of tile i - 1 (and tile i - 1)
-    if (s_restart) return true;
-    *(lds_u32x4*)(lds_ptr(s_p) + (w * 2 + 0) * 1024 + l * 16) = st.r.p[0];
-    *(lds_u32x4*)(lds_ptr(s_p) + (w * 2 + 1) * 1024 + l * 16) = st.r.p[1];
-    return false;
+    ovr |= __builtin_amdgcn_ballot_w64(st.r.overrun);
+    *(lds_u32x4*)(lds_ptr(s_p + (K & 1) * PBUF) + (w * 2 + 0) * 1024 + l * 16) = st.r.p[0];
+    *(lds_u32x4*)(lds_ptr(s_p + (K & 1) * PBUF) + (w * 2 + 1) * 1024 + l * 16) = st.r.p[1];
   };
 
 
@@ -444,34 +447,40 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int k = 0; k < CBW * RB; ++k) acc[k] = f32x16{};
     l_run = 0.f;
+    ovr = 0;
     if (pass > 0) prologue();
-    bool restart = false;
-    {
-      restart = vstep(Ic<0>{}, Ic<1>{}, 0, allow_restart);
-      for (int i = 1; i < n_tiles && !restart; i += 4) {
+    vstep(Ic<0>{}, Ic<1>{}, 0, allow_restart);
+    for (int i = 1; i < n_tiles; i += 4) {
 #define MLA_VSTEP(KK, D) \
-  if (!restart && i + D < n_tiles) restart = vstep(Ic<KK>{}, Ic<0>{}, i + D, allow_restart);
-        MLA_VSTEP(1, 0)
-        MLA_VSTEP(2, 1)
-        MLA_VSTEP(3, 2)
-        MLA_VSTEP(0, 3)
+  if (i + D < n_tiles) vstep(Ic<KK>{}, Ic<0>{}, i + D, allow_restart);
+      MLA_VSTEP(1, 0)
+      MLA_VSTEP(2, 1)
+      MLA_VSTEP(3, 2)
+      MLA_VSTEP(0, 3)
 #undef MLA_VSTEP
-      }
-      if (!restart) {
-        lds_barrier();  // P of the last tile everywhere
-        // the value MFMAs of the last tile, from buffer (n_tiles - 1) % 4 (one copy of
-        // the code: a branch per buffer would split the accumulators' registers)
-        const int kl = (n_tiles - 1) & 3;
-        const char* lt = kl == 0 ? s_tile0 : kl == 1 ? s_tile1 : kl == 2 ? s_tile2 : s_tile3;
-        pv(lt, [](int) {}, [](int) {}, Ic<0>{});
-      }
     }
-    wait_vm<0>();  // this wave's loads have landed (a restart leaves some in flight)
-    if (!restart) break;
+    // restart flags, in tile buffer (n_tiles + 1) % 4: its tile (n_tiles - 3) was last
+    // read in step n_tiles - 2, which every wave has left, or it was never used; no
+    // load targets it. (The P buffers may still be read by a slower wave's last step.)
+    const int kf = (n_tiles + 1) & 3;
+    int* s_flag = reinterpret_cast<int*>(kf == 0 ? s_tile0 : kf == 1 ? s_tile1 : kf == 2 ? s_tile2 : s_tile3);
+    if (l == 0) s_flag[w] = ovr != 0;
+    lds_barrier();  // P of the last tile and every wave's flag
+    bool restart = false;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) restart |= s_flag[k] != 0;  // uniform
+    if (!restart) {
+      // the value MFMAs of the last tile, from buffer (n_tiles - 1) % 4 (one copy of
+      // the code: a branch per buffer would split the accumulators' registers)
+      const int kl = (n_tiles - 1) & 3;
+      const char* lt = kl == 0 ? s_tile0 : kl == 1 ? s_tile1 : kl == 2 ? s_tile2 : s_tile3;
+      pv(lt, s_p + ((n_tiles - 1) & 1) * PBUF, [](int) {}, [](int) {}, Ic<0>{});
+      break;
+    }
     // restart the range with the largest score seen as every row's reference; the
-    // barrier orders every wave's drained loads and flag read before the reset
+    // barrier orders every wave's flag reads before the next pass writes P
+    wait_vm<0>();
     lds_barrier();
-    if (tid == 0) s_restart = 0;
     m_ref = m_seen;
   }
 
@@ -479,6 +488,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   //      its score wave; each wave stages its 32*CBW columns of all R rows in its
   //      own tile buffer ([R rows][4*CBW chunks], chunk ^ (row & 15)) and writes
   //      them out as contiguous row segments.
+  // 1 / l per row, in the P buffer the last tile did not use (free since the barrier
+  // after the last step; the staging below starts after the next barrier)
+  float* s_inv = reinterpret_cast<float*>(s_p + (n_tiles & 1) * PBUF + 16);
   if (l < 32) s_inv[r_own] = l_run > 0.f ? 1.f / l_run : 0.f;
   lds_barrier();  // every wave is past the last tile; s_inv complete
   constexpr int CPR = 4 * CBW;  // 16-byte chunks per staged row
