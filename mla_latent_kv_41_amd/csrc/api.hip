@@ -52,7 +52,8 @@ size_t elem_bytes(int dtype) { return dtype == MLA_F32 ? 4 : 2; }
 
 // Split plan for the bf16 path.
 struct Plan {
-  int nw;        // waves per attention workgroup (rows = 32 * nw)
+  int nw;        // 32-row blocks per attention workgroup (rows = 32 * nw)
+  bool roles;    // role-split 64-row form (rows not a multiple of 128)
   int hgroups;   // workgroups per (sequence, split)
   int n_splits;  // token ranges per sequence
   int chunk;     // tokens per range, a multiple of kTile
@@ -64,7 +65,10 @@ struct Plan {
 Plan plan_bf16(const Resolved& r, const mla_decode_args* a) {
   Plan p;
   const int rows = r.h * a->n_q;
-  p.nw = rows % 128 == 0 ? 4 : 2;
+  // 128-row workgroups when the rows come in 128s; else role-split 64-row workgroups
+  // (two score waves, two value waves)
+  p.roles = rows % 128 != 0;
+  p.nw = p.roles ? 2 : 4;
   p.hgroups = rows / (32 * p.nw);
   // one workgroup per CU either way: four tile buffers take most of the LDS
   const int64_t target = 256;
@@ -152,7 +156,6 @@ mla_status check_decode(const Resolved& r, const mla_decode_args* a) {
     if (rows % 64 != 0) return MLA_E_UNSUPPORTED;
     const int R = rows % 128 == 0 ? 128 : 64;
     if (R % a->n_q != 0 || r.h % (R / a->n_q) != 0) return MLA_E_UNSUPPORTED;
-    if (R == 64 && r.d_r != 0) return MLA_E_UNSUPPORTED;  // 64-row workgroups are position-free only
     if (a->gate_x && (a->d_model % (kGateSplit * 16) != 0 || (r.h * 128) % 128 != 0)) return MLA_E_UNSUPPORTED;
   }
   return MLA_OK;
@@ -251,6 +254,7 @@ mla_status decode_impl(const mla_dims* dims, const CacheRef& cache, const mla_de
   d.n_splits = p.n_splits;
   d.chunk = p.chunk;
   d.max_kv_len = a->max_kv_len;
+  d.role_split = p.roles ? 1 : 0;
   if (launch_decode_bf16(d, stream, a->ev_attn_begin, a->ev_attn_end) != hipSuccess) return MLA_E_HIP;
 
   CombineArgs c{};

@@ -21,14 +21,15 @@
 // columns 32*CBW*w .. +32*CBW of every row (Oᵀ accumulators, 16 blocks of 32x32
 // fp32 = 256 registers per lane, in AGPRs), so each cache element is transposed
 // out of LDS once per workgroup rather than once per wave. P travels between the
-// two through an 8 KiB LDS buffer, written in the B-operand order of the value
-// MFMA: the value MFMA takes the tile's 32 tokens in the order the score MFMA
-// leaves them in its accumulator. Two barriers per tile: one for the tile (and
-// the release of the previous tile and of P), one for P.
+// two through LDS, written in the B-operand order of the value MFMA: the value
+// MFMA takes the tile's 32 tokens in the order the score MFMA leaves them in its
+// accumulator.
 //
-// Pipelining: 128-row workgroups (one per CU) keep four tile buffers, so the
-// direct-to-LDS loads of a tile are issued three tiles before it is consumed;
-// 64-row workgroups run two per CU with two tile buffers each.
+// Pipelining: a workgroup (one per CU) keeps four tile buffers. Step i runs tile
+// i's scores and softmax together with tile i - 1's value MFMAs, with tile i + 1
+// in flight and tile i + 2 issued at its start; P is double-buffered by tile
+// parity, so each step needs one barrier. Query rows that do not come in 128s
+// take the role-split 64-row form further down.
 //
 // LDS tile layout: the 576 (or 512) columns are cut into groups of 64 (128 bytes,
 // eight 16-byte chunks); group G holds all 32 rows, row t at G*4096 + t*128, and
@@ -42,10 +43,11 @@
 // reference max is fixed at the first tile where the row sees a token, so the
 // accumulators never need rescaling: later P values may exceed 1, which is exact
 // in floating point as long as they stay in range. If a score ever exceeds the
-// reference by more than 64 (P > 2^64), the workgroup drains its loads and
-// restarts its token range with the largest score seen as the new reference (at
-// most 8 times). The decision is workgroup-uniform, through LDS flags read one
-// tile later, so every wave takes the same barriers.
+// reference by more than 64 (P > 2^64), the wave flags it; the waves exchange
+// their flags through LDS once after the range, and if any is set the workgroup
+// drains its loads and restarts the range with the largest score seen as every
+// row's reference (at most 8 times). The decision is workgroup-uniform, so every
+// wave takes the same barriers.
 //
 // Output per (b, split): the normalised partial O/l as bf16 rows of 512 (written
 // coalesced through LDS) and (m, l) in fp32; the combine kernel merges splits.
@@ -529,22 +531,379 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   }
 }
 
+// Role-split form for 64 query rows per workgroup (a (sequence, token range, head
+// group) unit of 64 rows). Waves 0-1 own the scores and the softmax of rows
+// 32w .. 32w + 31 (their Q_cat fragments in VGPRs, the same fragment order as the
+// 64-row workgroups above). Waves 2-3 own the value contraction for latent columns
+// 256 v .. 256 v + 255 (v = w - 2) of all 64 rows (Oᵀ: 16 blocks of 32x32 fp32 in
+// AGPRs) and issue every tile load. Both pairs run about 1.1k MFMA cycles per tile,
+// so the matrix cores of all four SIMDs stay busy, while a unit holds half the rows
+// of the 128-row form: a sequence needs half as many token ranges for the same
+// number of workgroups, which halves the split partials the combine reads back.
+//
+// Step i (one barrier): the value waves wait for their share of tile i, everyone
+// passes the barrier; the value waves issue tile i + 2 into the buffer of tile
+// i - 2 and run the value MFMAs of tile i - 1 (P from buffer (i - 1) % 2); the score
+// waves run tile i's score chain and softmax and publish P into buffer i % 2. P
+// buffer i % 2 held tile i - 2's P, which the value waves finished reading in step
+// i - 1. Restarts, masking and the output are as in the 128-row form.
+template <int DR>
+__global__ __launch_bounds__(256) void decode_roles_kernel(DecodeArgs a) {
+  constexpr int ROW = 512 + DR, ROWB = ROW * 2, CH = ROW / 8, KS = ROW / 16;
+  constexpr int R = 64;                           // query rows per workgroup
+  constexpr int TILE_BYTES = kTileT * ROWB;
+  constexpr int LOADS = (kTileT * CH) / 128;      // 16-byte loads per value-wave lane per tile
+  constexpr int CBW = 8;                          // value column blocks per value wave
+  constexpr int RB = 2;                           // row blocks of 32 query rows
+  static_assert((kTileT * CH) % 128 == 0, "tile loads per value wave");
+  static_assert(R * 256 * 2 <= TILE_BYTES, "a value wave's staged rows fit a tile buffer");
+  __shared__ __attribute__((aligned(1024))) char s_tile0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char s_tile1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char s_tile2[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char s_tile3[TILE_BYTES];
+  constexpr int PBUF = RB * 2 * 1024;  // P fragments [row block][k-step][lane]
+  __shared__ __attribute__((aligned(16))) char s_p[2 * PBUF];
+  static_assert(4 * TILE_BYTES + 2 * PBUF <= 160 * 1024, "LDS");
+  static_assert(16 + 4 * R <= PBUF, "1 / l fits a P buffer");
+
+  const int tid = threadIdx.x, l = tid % 64;
+  const int w = __builtin_amdgcn_readfirstlane(tid / 64);  // wave index, uniform
+  const bool scorer = w < 2;
+  const int vw = w - 2;  // value wave index (value waves only)
+  const int hgroups = (a.h * a.n_q) / R;
+  const int units = a.batch * a.n_splits * hgroups;
+  int u = blockIdx.x;
+  if ((units & 7) == 0) u = (blockIdx.x & 7) * (units >> 3) + (blockIdx.x >> 3);
+  const int hg = u % hgroups;
+  const int s = (u / hgroups) % a.n_splits;
+  const int b = u / (hgroups * a.n_splits);
+
+  const int kv = min(a.kv_lens[b], a.max_kv_len);
+  const int t_begin = s * a.chunk;
+  const int t_end = min(t_begin + a.chunk, kv);
+  if (t_begin >= t_end || kv < a.n_q) return;  // empty split: the combine skips it
+  const int n_tiles = (t_end - t_begin + kTileT - 1) / kTileT;
+
+  const int HG = R / a.n_q;  // heads per workgroup
+  const int r_own = 32 * (w & 1) + (l & 31);  // score waves: this lane's row
+  const int j_own = r_own / HG;
+  const int head_own = hg * HG + r_own % HG;
+  const int vis_own = kv - a.n_q + j_own;
+
+  // ---- tile loads (value waves): wave load n' = 2n + v fills LDS [n'*1024, +1024) =
+  //      column group n'/4, rows 8(n'%4) + l/8, chunk position l%8
+  uint32_t ld_lane[2];
+#pragma unroll
+  for (int odd = 0; odd < 2; ++odd) {
+    const int t = 8 * odd + (l >> 3);
+    ld_lane[odd] = static_cast<uint32_t>(t * ROWB + (((l & 7) ^ swz(t)) << 4));
+  }
+  const char* cache = static_cast<const char*>(a.cache.data);
+  const bool paged = a.cache.block_table != nullptr;
+  const __attribute__((address_space(4))) int32_t* table =
+      (const __attribute__((address_space(4))) int32_t*)(a.cache.block_table);
+  auto page_id = [&](int it) __attribute__((always_inline)) -> int {
+    const int blk = (t_begin + it * kTileT) / a.cache.block_size;
+    const int id = table[static_cast<int64_t>(b) * a.cache.max_blocks + blk];
+    return (id < 0 || id >= a.cache.n_blocks) ? 0 : id;
+  };
+  // ---- per-lane LDS read offsets (as in the 128-row form)
+  int sa_off[4];
+  {
+    const int t = l & 31, sw = swz(t);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) sa_off[kk] = t * 128 + (((2 * kk + (l >> 5)) ^ sw) << 4);
+  }
+  int va_off[2][2];
+  {
+    const int g = l >> 4, i = l & 15;
+#pragma unroll
+    for (int sec = 0; sec < 2; ++sec) {
+      const int t = 4 * (g >> 1) + (i >> 2) + 8 * sec;
+      const int sw = swz(t);
+#pragma unroll
+      for (int par = 0; par < 2; ++par) {
+        const int low = 2 * (g & 1) + ((i & 3) >> 1);
+        va_off[sec][par] = t * 128 + (((4 * par + low) ^ sw) << 4) + ((i & 1) << 3);
+      }
+    }
+  }
+
+  const int bound = min(t_end - 1, kv - a.n_q);
+  const int first_masked = bound - t_begin - (kTileT - 1) >= 0 ? (bound - t_begin - (kTileT - 1)) / kTileT + 1 : 0;
+  auto tile_ptr = [&](auto kc) __attribute__((always_inline)) -> char* {
+    constexpr int K = decltype(kc)::value;
+    if constexpr (K == 0) return s_tile0;
+    else if constexpr (K == 1) return s_tile1;
+    else if constexpr (K == 2) return s_tile2;
+    else return s_tile3;
+  };
+  const int64_t part_row0 = (static_cast<int64_t>(b) * a.n_splits + s) * a.n_q;
+
+  // The two roles run as separate copies of the loop (the branch is taken once, so
+  // the score waves' Q fragments and the value waves' accumulators never share a
+  // live range); both copies pass the same barriers in the same order.
+  auto run = [&](auto role) __attribute__((always_inline)) {
+    constexpr bool SC = decltype(role)::value != 0;
+    u32x4 qf[SC ? KS : 1];           // score waves: this row's Q_cat fragments
+    f32x16 acc[SC ? 1 : CBW * RB];   // value waves: Oᵀ, acc[cbl * RB + rb]
+    float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
+    uint64_t ovr = 0;
+    int pg_next = 0;
+
+    auto tile_rsrc = [&](int it) __attribute__((always_inline)) -> u32x4 {
+      const int t0 = t_begin + it * kTileT;
+      const char* base;
+      if (!paged) {
+        base = cache + (static_cast<int64_t>(b) * a.cache.t_max + t0) * ROWB;
+      } else {
+        base = cache + (static_cast<int64_t>(pg_next) * a.cache.block_size + t0 % a.cache.block_size) * ROWB;
+        if (it + 1 < n_tiles) pg_next = page_id(it + 1);
+      }
+      const uint64_t ba = reinterpret_cast<uint64_t>(base);
+      const uint32_t rows = static_cast<uint32_t>(min(kTileT, t_end - t0));
+      return u32x4{static_cast<uint32_t>(ba), static_cast<uint32_t>(ba >> 32) & 0xFFFFu,
+                   rows * static_cast<uint32_t>(ROWB), 0x00020000u};
+    };
+    auto issue_tile = [&](int it, char* tile) __attribute__((always_inline)) {
+      const u32x4 rsrc = tile_rsrc(it);
+#pragma unroll
+      for (int n = 0; n < LOADS; ++n) {
+        const int np = 2 * n + vw;  // wave-uniform
+        const int G = np >> 2, rq = np & 3;
+        dma_b128(rsrc, ld_lane[rq & 1], static_cast<uint32_t>(G * 128 + (rq >> 1) * 16 * ROWB),
+                 static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_ptr(tile) + np * 1024)));
+      }
+    };
+    constexpr int SDEPTH = 6;
+    auto scores = [&](const char* tile) __attribute__((always_inline)) {
+      f32x16 sc = {};
+      u32x4 fa[SDEPTH];
+      auto frag = [&](int ks) __attribute__((always_inline)) {
+        return *(lds_u32x4*)(lds_ptr(tile) + sa_off[ks & 3] + (ks >> 2) * 4096);
+      };
+#pragma unroll
+      for (int ks = 0; ks < SDEPTH; ++ks) fa[ks] = frag(ks);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) mfma_v(sc, fa[ks % SDEPTH], qf[ks]);
+        else mfma_v_last(sc, fa[ks % SDEPTH], qf[ks]);
+        if (ks + SDEPTH < KS) fa[ks % SDEPTH] = frag(ks + SDEPTH);
+      }
+      return sc;
+    };
+    auto apply_mask = [&](f32x16& sc, int it) __attribute__((always_inline)) {
+      const int t0 = t_begin + it * kTileT;
+      const int lim = min(t_end - 1, vis_own);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int tok = t0 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
+        sc[v] = tok > lim ? -INFINITY : sc[v];
+      }
+    };
+    // softmax of a tile against the row's fixed reference: P as 8 packed bf16 pairs
+    // (values 2k, 2k + 1 of the score accumulator); `overrun` if a score passed it by
+    // more than the headroom
+    auto softmax = [&](const f32x16& sc, bool allow_restart, u32x4* p) __attribute__((always_inline)) -> bool {
+      const float m0 = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      const float m1 = fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7]));
+      const float m2 = fmaxf(fmaxf(sc[8], sc[9]), fmaxf(sc[10], sc[11]));
+      const float m3 = fmaxf(fmaxf(sc[12], sc[13]), fmaxf(sc[14], sc[15]));
+      const float mx = half_max(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)));
+      m_seen = fmaxf(m_seen, mx);
+      if (m_ref == -INFINITY) m_ref = mx;  // first tile where the row sees a token
+      const bool overrun = allow_restart && mx > m_ref + kHeadroom;
+      const float mref = m_ref == -INFINITY ? 0.f : m_ref;
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float p0 = fast_exp2(sc[2 * q] - mref), p1 = fast_exp2(sc[2 * q + 1] - mref);
+        p[q >> 2][q & 3] = pack_bf16x2(p0, p1);
+        ps[q & 3] += p0 + p1;
+      }
+      l_run += half_sum((ps[0] + ps[1]) + (ps[2] + ps[3]));
+      return overrun;
+    };
+    // value MFMAs of one tile: this value wave's 8 column blocks x both row blocks,
+    // P from LDS one k-step at a time, the transposed cache fragments through a
+    // four-deep window
+    auto pv = [&](const char* tile, const char* pbuf) __attribute__((always_inline)) {
+      auto load = [&](int f) __attribute__((always_inline)) {
+        const int kk = f / CBW, cb = CBW * vw + f % CBW;
+        lds_char* tb = lds_ptr(tile) + kk * 16 * 128 + (cb >> 1) * 4096;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tb + va_off[0][cb & 1]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tb + va_off[1][cb & 1]));
+        const i16x8 af = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return af;
+      };
+      constexpr int NF = 2 * CBW, WIN = 4;
+      i16x8 frag[WIN];
+#pragma unroll
+      for (int f = 0; f < WIN; ++f) frag[f] = load(f);
+      u32x4 pb[RB];
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int kk = f / CBW, cbl = f % CBW;
+        if (cbl == 0) {
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) pb[rb] = *(lds_u32x4*)(lds_ptr(pbuf) + (rb * 2 + kk) * 1024 + l * 16);
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          acc[cbl * RB + rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, frag[f % WIN]), as_bf16x8(pb[rb]), acc[cbl * RB + rb], 0, 0, 0);
+          if (rb == RB - 1 && f + WIN < NF) frag[f % WIN] = load(f + WIN);
+        }
+      }
+    };
+    auto vstep = [&](auto kc, auto first, int i, bool allow_restart) __attribute__((always_inline)) {
+      constexpr int K = decltype(kc)::value;
+      constexpr bool FIRST = decltype(first)::value != 0;
+      if constexpr (!SC) {
+        if (i + 1 < n_tiles) wait_vm<LOADS>();  // tile i has landed (tile i + 1 in flight)
+        else wait_vm<0>();
+      }
+      lds_barrier();  // tile i and P of tile i - 1 everywhere; tile i - 2 is free
+      if constexpr (!SC) {
+        if (i + 2 < n_tiles) issue_tile(i + 2, tile_ptr(Ic<(K + 2) % 4>{}));
+        if constexpr (!FIRST) pv(tile_ptr(Ic<(K + 3) % 4>{}), s_p + ((K + 1) & 1) * PBUF);
+      } else {
+        f32x16 sc = scores(tile_ptr(kc));
+        if (i >= first_masked) apply_mask(sc, i);  // uniform
+        u32x4 p[2];
+        const bool overrun = softmax(sc, allow_restart, p);
+        ovr |= __builtin_amdgcn_ballot_w64(overrun);
+        *(lds_u32x4*)(lds_ptr(s_p + (K & 1) * PBUF) + (w * 2 + 0) * 1024 + l * 16) = p[0];
+        *(lds_u32x4*)(lds_ptr(s_p + (K & 1) * PBUF) + (w * 2 + 1) * 1024 + l * 16) = p[1];
+      }
+    };
+    auto prologue = [&]() __attribute__((always_inline)) {
+      if constexpr (!SC) {
+        if (paged) pg_next = page_id(0);
+        if (0 < n_tiles) issue_tile(0, s_tile0);
+        if (1 < n_tiles) issue_tile(1, s_tile1);
+      }
+    };
+
+    prologue();
+    if constexpr (SC) {
+      const u32x4* qp = reinterpret_cast<const u32x4*>(a.q_cat) +
+                        ((static_cast<int64_t>(b) * hgroups + hg) * 2 + w) * KS * 64 + l;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = qp[ks * 64];
+      wait_vm<0>();
+    }
+    for (int pass = 0;; ++pass) {
+      const bool allow_restart = pass < kMaxRestarts;
+      if constexpr (!SC) {
+#pragma unroll
+        for (int k = 0; k < CBW * RB; ++k) acc[k] = f32x16{};
+      }
+      l_run = 0.f;
+      ovr = 0;
+      if (pass > 0) prologue();
+      vstep(Ic<0>{}, Ic<1>{}, 0, allow_restart);
+      for (int i = 1; i < n_tiles; i += 4) {
+#define MLA_RSTEP(KK, D) \
+  if (i + D < n_tiles) vstep(Ic<KK>{}, Ic<0>{}, i + D, allow_restart);
+        MLA_RSTEP(1, 0)
+        MLA_RSTEP(2, 1)
+        MLA_RSTEP(3, 2)
+        MLA_RSTEP(0, 3)
+#undef MLA_RSTEP
+      }
+      // restart flags in tile buffer (n_tiles + 1) % 4 (its tile was last read in step
+      // n_tiles - 2, or never used; no load targets it)
+      const int kf = (n_tiles + 1) & 3;
+      int* s_flag = reinterpret_cast<int*>(kf == 0 ? s_tile0 : kf == 1 ? s_tile1 : kf == 2 ? s_tile2 : s_tile3);
+      if (l == 0) s_flag[w] = ovr != 0;
+      lds_barrier();  // P of the last tile and every wave's flag
+      const bool restart = (s_flag[0] | s_flag[1]) != 0;  // the score waves' flags; uniform
+      if (!restart) {
+        if constexpr (!SC) {
+          const int kl = (n_tiles - 1) & 3;
+          const char* lt = kl == 0 ? s_tile0 : kl == 1 ? s_tile1 : kl == 2 ? s_tile2 : s_tile3;
+          pv(lt, s_p + ((n_tiles - 1) & 1) * PBUF);
+        }
+        break;
+      }
+      if constexpr (!SC) wait_vm<0>();
+      lds_barrier();  // every wave's flag reads are done before the next pass writes P
+      m_ref = m_seen;
+    }
+
+    // ---- epilogue: 1 / l of each row from the score waves; each value wave stages
+    //      its 256 columns of the 64 rows in tile buffer v ([64 rows][32 chunks],
+    //      chunk ^ (row & 31)) and writes them out as contiguous 512-byte row segments
+    float* s_inv = reinterpret_cast<float*>(s_p + (n_tiles & 1) * PBUF + 16);
+    if constexpr (SC) {
+      if (l < 32) s_inv[r_own] = l_run > 0.f ? 1.f / l_run : 0.f;
+    }
+    lds_barrier();  // every wave is past the last tile; s_inv complete
+    if constexpr (!SC) {
+      constexpr int CPR = 4 * CBW;   // 16-byte chunks per staged row (32)
+      constexpr int RSB = 16 * CPR;  // staged row bytes (512)
+      char* stg = vw == 0 ? s_tile0 : s_tile1;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int row = 32 * rb + (l & 31);
+        const float inv = s_inv[row];
+#pragma unroll
+        for (int cbl = 0; cbl < CBW; ++cbl)
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) {
+            const f32x16& o = acc[cbl * RB + rb];
+            const int chunk = (4 * cbl + v4) ^ (row & 31);
+            const u32x2 v2 = {pack_bf16x2(o[4 * v4] * inv, o[4 * v4 + 1] * inv),
+                              pack_bf16x2(o[4 * v4 + 2] * inv, o[4 * v4 + 3] * inv)};
+            *(lds_u32x2*)(lds_ptr(stg) + row * RSB + chunk * 16 + (l >> 5) * 8) = v2;
+          }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging writes are done
+      __builtin_amdgcn_wave_barrier();
+      constexpr int RPI = 64 / CPR;  // rows per wave instruction (2)
+#pragma unroll 4
+      for (int q = 0; q < R / RPI; ++q) {
+        const int row = RPI * q + l / CPR, ch = l % CPR;
+        const int j = row / HG, head = hg * HG + row % HG;
+        const u32x4 v = *(lds_u32x4*)(lds_ptr(stg) + row * RSB + ((ch ^ (row & 31)) << 4));
+        *reinterpret_cast<u32x4*>(a.o_part + ((part_row0 + j) * a.h + head) * 512 + 256 * vw + ch * 8) = v;
+      }
+    } else {
+      if (l < 32) {
+        float* ml = a.ml_part + ((part_row0 + j_own) * a.h + head_own) * 2;
+        ml[0] = m_ref;
+        ml[1] = l_run;
+      }
+    }
+  };
+  if (scorer) run(Ic<1>{});
+  else run(Ic<0>{});
+}
+
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   // hipExtLaunchKernelGGL stamps ev0/ev1 from the dispatch itself, so an event pair
   // brackets exactly this kernel's execution (null events: plain launch).
   const int rows = a.h * a.n_q;
-  if (rows % 128 == 0) {
-    const unsigned units = static_cast<unsigned>(a.batch * a.n_splits * (rows / 128));
-    if (a.d_r == 64)
-      hipExtLaunchKernelGGL(decode_kernel<4, 64>, dim3(units), dim3(256), 0, s, ev0, ev1, 0, a);
-    else
-      hipExtLaunchKernelGGL(decode_kernel<4, 0>, dim3(units), dim3(256), 0, s, ev0, ev1, 0, a);
-  } else {
-    // 64 query rows per workgroup (e.g. 64 heads, one query): position-free rows only
-    if (a.d_r != 0) return hipErrorInvalidValue;
+  if (a.role_split) {
+    if (rows % 64 != 0) return hipErrorInvalidValue;
     const unsigned units = static_cast<unsigned>(a.batch * a.n_splits * (rows / 64));
-    hipExtLaunchKernelGGL(decode_kernel<2, 0>, dim3(units), dim3(128), 0, s, ev0, ev1, 0, a);
+    if (a.d_r == 64)
+      hipExtLaunchKernelGGL(decode_roles_kernel<64>, dim3(units), dim3(256), 0, s, ev0, ev1, 0, a);
+    else if (a.d_r == 0)
+      hipExtLaunchKernelGGL(decode_roles_kernel<0>, dim3(units), dim3(256), 0, s, ev0, ev1, 0, a);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
   }
+  if (rows % 128 != 0) return hipErrorInvalidValue;
+  const unsigned units = static_cast<unsigned>(a.batch * a.n_splits * (rows / 128));
+  if (a.d_r == 64)
+    hipExtLaunchKernelGGL(decode_kernel<4, 64>, dim3(units), dim3(256), 0, s, ev0, ev1, 0, a);
+  else if (a.d_r == 0)
+    hipExtLaunchKernelGGL(decode_kernel<4, 0>, dim3(units), dim3(256), 0, s, ev0, ev1, 0, a);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

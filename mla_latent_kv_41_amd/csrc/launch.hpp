@@ -44,6 +44,7 @@ struct DecodeArgs {
   uint16_t* o_part;       // [B][S][n_q][h][512] bf16, normalised O / l
   float* ml_part;         // [B][S][n_q][h][2]
   int32_t batch, n_q, h, d_r, n_splits, chunk, max_kv_len;
+  int32_t role_split;   // 1: role-split 64-row workgroups (h n_q % 128 == 64); 0: 128-row workgroups
 };
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 

@@ -73,7 +73,7 @@ def test_rejections_happen_on_the_host():
     assert call_decode(ds_dims(), host=[4097] * 31 + [5000])[0] == mla.MLA_E_SHAPE
     assert call_decode(ds_dims(), host=[0] + [4097] * 31)[0] == mla.MLA_E_SHAPE  # kv_len < n_q
     assert call_decode(ds_dims(n_heads=96))[0] == mla.MLA_E_UNSUPPORTED       # 96 rows per step
-    assert call_decode(ds_dims(n_heads=64), batch=16)[0] == mla.MLA_E_UNSUPPORTED  # 64 rows need d_rope 0
+    assert call_decode(ds_dims(n_heads=64), batch=16)[0] == mla.MLA_OK             # 64-row groups, with RoPE
     assert call_decode(ds_dims(n_heads=64, d_rope=0), batch=16)[0] == mla.MLA_OK
     assert call_decode(ds_dims(), num_splits=-1)[0] == mla.MLA_E_SHAPE
     assert call_decode(ds_dims(), gate=True, d_model=100)[0] == mla.MLA_E_UNSUPPORTED

@@ -188,6 +188,49 @@ def test_error_bound_holds_on_short_ragged_sequences():
     assert np.max(err / bound) <= 1.0
 
 
+@pytest.mark.parametrize("cid,batch,splits", [(2, 40, 6), (4, 20, 5)])
+def test_combine_row_blocks_with_uneven_splits(cid, batch, splits):
+    """40 query rows: three 16-row combine blocks (the last holds 8). Lengths are spread
+    so the rows of one block hold different numbers of splits, and the partials of
+    splits past a row's last one are poisoned (NaN). Every output against the
+    first-order bf16 bound, and lse."""
+    if cid == 2:
+        w = synth.make_workload(2, batch=batch, ctx=900)
+        w.kv_lens = np.linspace(40, 901, batch).astype(np.int32)
+    else:
+        w = synth.make_workload(4, batch=batch, ctx_range=(30, 900))
+    say("case %d B=%d n_q=%d kv=[%d..%d] splits=%d" % (cid, w.batch, w.n_q, w.kv_lens.min(), w.kv_lens.max(), splits))
+    t = synth.draw(w)
+    step = GpuStep(w, t)
+    step.decode(num_splits=splits)
+    step.workspace.fill_(255)  # 0xFFFF bf16 / fp32 words are NaN: the partials no split writes
+    out = step.decode(num_splits=splits).cpu().numpy().astype(np.float64)
+    ref, lse = oracle_out(w, t, want_lse=True)
+    bound = bf16_error_bound(w, t)
+    err = np.abs(out - ref)
+    say("  max err/bound %.3f, max-abs/rms %.4f" % (float(np.max(err / bound)), err.max() / np.sqrt(np.mean(ref ** 2))))
+    assert np.all(np.isfinite(out))
+    assert np.max(err / bound) <= 1.0
+    assert np.max(np.abs(step.lse.cpu().numpy() - lse)) <= 1e-2
+
+
+@pytest.mark.parametrize("cid,h,batch", [(2, 64, 4), (4, 32, 3), (4, 96, 2)])
+def test_64_row_groups_with_rope(cid, h, batch):
+    """Head counts whose query rows (h x n_q) are not a multiple of 128 take 64-row
+    workgroups (64 heads x 1 query, 32 heads x 2 queries, or three groups of 32 heads
+    x 2 queries), here with the decoupled RoPE key: every output and lse."""
+    w = synth.make_workload(cid, batch=batch, ctx=700) if cid == 2 else \
+        synth.make_workload(cid, batch=batch, ctx_range=(300, 900))
+    w.h = h
+    say("case %d h=%d B=%d n_q=%d kv=[%d..%d]" % (cid, h, w.batch, w.n_q, w.kv_lens.min(), w.kv_lens.max()))
+    t = synth.draw(w)
+    step = GpuStep(w, t)
+    out = step.decode().cpu().numpy().astype(np.float64)
+    ref, lse = oracle_out(w, t, want_lse=True)
+    check_bf16(out, ref, what="h=%d n_q=%d" % (h, w.n_q))
+    assert np.max(np.abs(step.lse.cpu().numpy() - lse)) <= 1e-2
+
+
 def test_split_count_does_not_change_the_result():
     w = synth.make_workload(2, batch=2, ctx=2000)
     t = synth.draw(w)
