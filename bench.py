@@ -344,7 +344,9 @@ def main():
                 "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "mfma_TFLOPs": round(attn_tflops, 1),
                 "mfma_frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
-    roof.update({"kernel": "decode_kernel (split-K attention over the latent cache)",
+    rows = w.h * w.n_q
+    form = "128-row workgroups" if rows % 128 == 0 else "role-split 64-row workgroups"
+    roof.update({"kernel": "split-K attention over the latent cache (%s)" % form,
                  "algorithmic_bytes_per_launch": cache_bytes, "algorithmic_flops_per_launch": attn_flops})
     out = {
         "metric": "MLA decode TFLOP/s + latent-cache GB/s (% roofline), h=128 B=32 ctx=4096",
