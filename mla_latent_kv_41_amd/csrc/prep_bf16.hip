@@ -161,6 +161,20 @@ __global__ __launch_bounds__(512) void qprep_kernel(QPrepArgs a) {
   // ================= the product: waves 0-3, head hw =================
   const int hw = min(i0 + w, a.h - 1);  // past h: a discarded copy
   char* area = s_area[w];
+  // q_nope rows 32mb .. +31 of head hw, whole rows: load i, lane l -> row 4i + l/16,
+  // 16-byte chunk l%16 -> area[row][chunk]
+  u32x4 rows[8];
+  auto load_rows = [&](int mb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int m = 32 * mb + 4 * i + (l >> 4);
+      rows[i] = m < a.M ? *reinterpret_cast<const u32x4*>(a.q_nope + (static_cast<int64_t>(m) * a.h + hw) * 128 + 8 * (l & 15))
+                        : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  // the first block's rows go out before the weights, so they land first and the
+  // products can follow the weights as they arrive
+  load_rows(0);
   // W_UK fragments of head hw: column blocks 2nb, 2nb + 1, 8 k-steps each
   u32x4 bfr[2][8];
 #pragma unroll
@@ -169,16 +183,9 @@ __global__ __launch_bounds__(512) void qprep_kernel(QPrepArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) bfr[cb][ks] = wk[ks * 64];
   }
+  __builtin_amdgcn_sched_barrier(0);  // every weight load issued before the rows' wait
   for (int mb = 0; mb * 32 < a.M; ++mb) {
-    // q_nope rows 32mb .. +31 of head hw, whole rows: load i, lane l -> row 4i + l/16,
-    // 16-byte chunk l%16 -> area[row][chunk]
-    u32x4 rows[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int m = 32 * mb + 4 * i + (l >> 4);
-      rows[i] = m < a.M ? *reinterpret_cast<const u32x4*>(a.q_nope + (static_cast<int64_t>(m) * a.h + hw) * 128 + 8 * (l & 15))
-                        : u32x4{0u, 0u, 0u, 0u};
-    }
+    if (mb > 0) load_rows(mb);
 #pragma unroll
     for (int i = 0; i < 8; ++i) *(lds_u32x4*)(lds_ptr(area) + (4 * i + (l >> 4)) * kQnB + (l & 15) * 16) = rows[i];
     // B fragment k-step ks: row l%32, k = 16ks + 8(l/32) + e
