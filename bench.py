@@ -146,6 +146,8 @@ def cpu_baseline(w, t, budget_s=12.0):
 
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out>/prof_ds -o ds -- "
              "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline")
+TRACE_CMD_CFG = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out>/prof_c{c} -o c{c} -- "
+                 "python3 bench.py --config {c} --steps 10 --warmup 3 --no-cpu-baseline")
 PMC_CMD = ("rocprofv3 --pmc {c} --output-format csv -d <out>/pmc/{c} -o {c} -- "
            "python3 bench.py --steps 4 --warmup 2 --no-cpu-baseline --calibrate-copy")
 COPY_BYTES = 512 << 20
@@ -245,6 +247,27 @@ def summarize_profiles(d):
            "fetch_bytes_per_launch": int(fetch_b), "write_bytes_per_launch": int(write_b),
            "bytes_per_launch": int(fetch_b + write_b)}
     json.dump(rec, open(os.path.join(prof, "attention_traffic.json"), "w"), indent=1)
+    # kernel traces of the other workloads, where DIR holds them (DIR/prof_c<N>, log
+    # DIR/prof_c<N>.log)
+    for c in (3, 4, 5):
+        tdir = os.path.join(d, "prof_c%d" % c)
+        if not os.path.isdir(tdir):
+            continue
+        line = _bench_line(tdir + ".log")
+        wl = line["config"]["workload"]
+        stats = list(csv.DictReader(open(glob.glob(os.path.join(tdir, "*kernel_stats.csv"))[0])))
+        lines = ["# Kernel trace: %s (`bench.py --config %d`)" % (wl, c), "",
+                 "Command (from /tmp with TMPDIR=/tmp):", "", "    " + TRACE_CMD_CFG.format(c=c), "",
+                 "Attention kernel: %s. Bench line of the traced run: %.1f TFLOP/s, %.1f us per step "
+                 "(under the tracer)." % (line["roofline"]["kernel"], line["value"], line["ms_per_step"] * 1e3), "",
+                 "| kernel | calls | average us | min us | max us | share |", "|---|---|---|---|---|---|"]
+        for r in stats:
+            lines.append("| `%s` | %s | %.2f | %.2f | %.2f | %.1f%% |" % (
+                short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+        lines += ["", "Attention kernel source sha256 (mla_latent_kv_41_amd/csrc/decode_bf16.hip + common.hpp): `%s`"
+                  % line["attention_kernel_source_sha256"], ""]
+        open(os.path.join(prof, "decode_step_%s_kernel_trace.md" % wl), "w").write("\n".join(lines))
     print("summaries written for attention kernel source %s" % sha)
 
 

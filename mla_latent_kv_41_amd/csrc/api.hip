@@ -60,6 +60,7 @@ struct Plan {
   int comb_rows;    // combine: query rows per workgroup (<= 32)
   int comb_splits;  // combine: partial half rows staged per row and batch
   int comb_slots;   // combine: staged half rows per batch (256, or 128 with two workgroups per CU)
+  bool ragged;      // host lengths given and not all equal
 };
 
 Plan plan_bf16(const Resolved& r, const mla_decode_args* a) {
@@ -103,6 +104,11 @@ Plan plan_bf16(const Resolved& r, const mla_decode_args* a) {
   p.comb_rows = std::min(p.comb_slots == 128 ? 16 : 32, M);
   while (p.comb_rows > 1 && 2LL * r.h * ((M + p.comb_rows - 1) / p.comb_rows) < 256) p.comb_rows = (p.comb_rows + 1) / 2;
   p.comb_splits = std::min(p.n_splits, p.comb_slots / p.comb_rows);
+  // ragged lengths: the combine reads the lengths before staging partial rows, so the
+  // rows of short sequences load only the splits that hold their tokens
+  p.ragged = false;
+  if (a->kv_lens_host)
+    for (int b = 1; b < a->batch; ++b) p.ragged |= a->kv_lens_host[b] != a->kv_lens_host[0];
   return p;
 }
 
@@ -274,6 +280,7 @@ mla_status decode_impl(const mla_dims* dims, const CacheRef& cache, const mla_de
   c.rows_per_wg = p.comb_rows;
   c.splits_per_batch = p.comb_splits;
   c.slots = p.comb_slots;
+  c.lengths_first = p.ragged ? 1 : 0;
   return launch_combine_bf16(c, stream) == hipSuccess ? MLA_OK : MLA_E_HIP;
 }
 

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   __shared__ __attribute__((aligned(1024))) char s_part[kSlots * kSlotBytes];
   __shared__ __attribute__((aligned(16))) float s_ml[kMlCap * 2];  // (m, l) of (row, split)
   __shared__ float s_w[kSlots];     // weight of each staged half row
-  __shared__ int s_kv[32];          // per row: sequence length
+  __shared__ int s_kv[64];          // per row: sequence length (the load writes all 64 lanes)
   __shared__ int s_ns[32];          // per row: number of splits holding its tokens
   __shared__ float s_stat[32][2];   // per row: max M and 1 / L
   const int i = blockIdx.x, kh = blockIdx.y, mb = blockIdx.z;
@@ -83,7 +83,11 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     for (int k = 0; k < kStageLoads; ++k) {  // a loop: this code runs once per workgroup,
                                               // so its size costs instruction fetches
       const int sp = s0 + q;
-      const bool ok = r < rows && sp < NS;
+      bool ok = r < rows && sp < NS;
+      if (a.lengths_first && ok) {  // uniform; the row's length is in LDS already
+        const int kv = min(s_kv[r], a.max_kv_len);
+        ok = kv >= a.n_q && sp * a.chunk < kv;
+      }
       const int64_t row0 = ((static_cast<int64_t>(b) * NS) * a.n_q + j) * a.h + i;  // split 0
       const uint32_t off = ok ? static_cast<uint32_t>(row0 * 1024 + sp * split_stride + kh * kHalf * 2 + cl * 16) : kOobOffset;
       dma_b128(rs_part, off, 0u, lds_addr(s_part) + (w + 4 * k) * 2 * kSlotBytes);
@@ -94,7 +98,9 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     }
   };
 
-  // ---- loads: sequence lengths (wave 0), (m_s, l_s) of all rows x splits, batch 0
+  // ---- loads: sequence lengths (wave 0), (m_s, l_s) of all rows x splits, batch 0.
+  //      Ragged batches wait for the lengths first, so that the partial rows of
+  //      splits past a row's last one are not loaded at all (they read as zeros).
   {
     const u32x4 rs_ml = buffer_rsrc(a.ml_part, static_cast<uint32_t>(
         static_cast<int64_t>(a.batch) * NS * a.n_q * a.h * 2 * 4));
@@ -108,6 +114,10 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
       const int r = pi / NS, sp = pi - r * NS;
       const uint32_t off = f < nf ? static_cast<uint32_t>((part_row(m0 + r, sp) * 2 + (f & 1)) * 4) : kOobOffset;
       dma_b32(rs_ml, off, lds_addr(s_ml) + 64 * q * 4);
+    }
+    if (a.lengths_first) {
+      wait_vm<0>();
+      lds_barrier();  // the lengths, for every wave
     }
     stage(0);
   }
@@ -235,6 +245,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   // wave issues a fixed number of loads): zero them, so the merge can take every
   // slot of a batch with weight 0 there
   auto clear_stale = [&](int s0) __attribute__((always_inline)) {
+    if (a.lengths_first) return;  // those slots were loaded as zeros
     if (!__builtin_amdgcn_ballot_w64(l < rows && ns_lane < s0 + min(SB, NS - s0))) return;  // uniform
     for (int e = tid; e < rows * SB * 32; e += 256) {  // 16-byte pieces
       const int slot = e >> 5, r = slot / SB, sp = s0 + slot - r * SB;

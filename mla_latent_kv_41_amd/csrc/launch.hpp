@@ -60,6 +60,8 @@ struct CombineArgs {
   int32_t rows_per_wg;       // query rows per workgroup, 1..32
   int32_t splits_per_batch;  // half partial rows staged per row and batch (rows * splits <= slots)
   int32_t slots;             // staged half rows per batch: 256, or 128 (two workgroups per CU)
+  int32_t lengths_first;     // 1: wait for the sequence lengths before staging, and skip the
+                             // partial rows of splits past each row's last one (ragged batches)
 };
 hipError_t launch_combine_bf16(const CombineArgs& a, hipStream_t s);
 
