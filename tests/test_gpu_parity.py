@@ -127,9 +127,13 @@ def bf16_error_bound(w, t):
     kr = oracle.cache_keys(d_r=w.d_r, k_r=t["k_r"], kv_lens=w.kv_lens) if w.d_r else None
     qs = w.scale * np.log2(np.e)
     bound = np.zeros((w.batch, w.n_q, w.h * w.d_v))
+    wuv_flat = wuv.reshape(w.d_c, w.h * w.d_v)
+    wuv_abs = np.abs(wuv).transpose(1, 0, 2)                               # [h, d_c, d_v]
     for b in range(w.batch):
         T = int(w.kv_lens[b])
         C = np.concatenate([c[b, :T], kr[b, :T]], 1) if w.d_r else c[b, :T]
+        # values of every visible token, all heads: [h, t, d_v] (one product per sequence)
+        V_all = (c[b, :T] @ wuv_flat).reshape(T, w.h, w.d_v).transpose(1, 0, 2)
         for j in range(w.n_q):
             pos = T - w.n_q + j
             qa = np.einsum("hd,chd->hc", qn[b, j], wuk)
@@ -142,11 +146,11 @@ def bf16_error_bound(w, t):
             p = np.exp2(S - S.max(1, keepdims=True))
             p /= p.sum(1, keepdims=True)
             olat = p @ c[b, :pos + 1]                                      # [h, d_c]
-            V = np.einsum("tc,chd->htd", c[b, :pos + 1], wuv)              # [h, t, d_v]
-            o = np.einsum("ht,htd->hd", p, V)
-            dev = np.einsum("ht,htd->hd", p, np.abs(V - o[:, None, :]))
+            V = V_all[:, :pos + 1]                                         # [h, t, d_v]
+            o = np.matmul(p[:, None, :], V)[:, 0]                          # [h, d_v]
+            dev = np.matmul(p[:, None, :], np.abs(V - o[:, None, :]))[:, 0]
             pert = dev * (np.log(2) * 2 * E.max(1, keepdims=True) + 2.0 ** -7)
-            part = 2.0 ** -8 * np.einsum("hc,chd->hd", np.abs(olat), np.abs(wuv))
+            part = 2.0 ** -8 * np.matmul(np.abs(olat)[:, None, :], wuv_abs)[:, 0]
             bound[b, j] = (pert + part).reshape(-1)
     return bound
 
@@ -188,17 +192,17 @@ def test_error_bound_holds_on_short_ragged_sequences():
     assert np.max(err / bound) <= 1.0
 
 
-@pytest.mark.parametrize("cid,batch,splits", [(2, 40, 6), (4, 20, 5)])
-def test_combine_row_blocks_with_uneven_splits(cid, batch, splits):
-    """40 query rows: three 16-row combine blocks (the last holds 8). Lengths are spread
-    so the rows of one block hold different numbers of splits, and the partials of
-    splits past a row's last one are poisoned (NaN). Every output against the
-    first-order bf16 bound, and lse."""
+@pytest.mark.parametrize("cid,batch,splits,ctx", [(2, 40, 6, 900), (4, 20, 5, 900), (2, 72, 6, 200), (4, 36, 5, 200)])
+def test_combine_row_blocks_with_uneven_splits(cid, batch, splits, ctx):
+    """40 or 72 query rows: three or five 16-row combine blocks (the last holds 8).
+    Lengths are spread so the rows of one block hold different numbers of splits, and
+    the partials of splits past a row's last one are poisoned (NaN). Every output
+    against the first-order bf16 bound, and lse."""
     if cid == 2:
-        w = synth.make_workload(2, batch=batch, ctx=900)
-        w.kv_lens = np.linspace(40, 901, batch).astype(np.int32)
+        w = synth.make_workload(2, batch=batch, ctx=ctx)
+        w.kv_lens = np.linspace(40, ctx + 1, batch).astype(np.int32)
     else:
-        w = synth.make_workload(4, batch=batch, ctx_range=(30, 900))
+        w = synth.make_workload(4, batch=batch, ctx_range=(30, ctx))
     say("case %d B=%d n_q=%d kv=[%d..%d] splits=%d" % (cid, w.batch, w.n_q, w.kv_lens.min(), w.kv_lens.max(), splits))
     t = synth.draw(w)
     step = GpuStep(w, t)
@@ -321,10 +325,10 @@ def test_large_score_jump_restarts_the_range():
     check_bf16(out, ref, what="all heads after a score jump")
 
 
-@pytest.mark.parametrize("batch,d_model", [(40, 8192), (3, 2048)])
+@pytest.mark.parametrize("batch,d_model", [(40, 8192), (72, 4096), (3, 2048)])
 def test_gate_row_blocks_and_widths(batch, d_model):
     """The gate GEMM over more than one 32-row block of queries, with K splits of 512
-    rows (two staged chunks) or 128 rows (one partial chunk)."""
+    rows (two staged chunks), 256 rows or 128 rows (one partial chunk)."""
     w = synth.make_workload(5, batch=batch, ctx=100)
     w.d_model = d_model
     t = synth.draw(w)
