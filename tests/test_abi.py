@@ -120,3 +120,18 @@ def test_split_plan_sizes():
             q_cat = 4 * 128 * 576 * 2
             parts = 4 * splits * 128 * (512 * 2 + 2 * 4)
             assert q_cat + parts <= n <= q_cat + parts + 3 * 256
+
+
+def test_split_plan_64_row_groups():
+    """64 heads x 1 query (with or without the RoPE key) plan 64-row units: a
+    sequence gets 256 / batch token ranges, each holding 64 partial rows."""
+    for d_rope in (64, 0):
+        d = ds_dims(n_heads=64, d_rope=d_rope)
+        st, n = call_decode(d, batch=16, max_kv_len=65537, t_max=65537)
+        assert st == mla.MLA_OK
+        chunk = -(-(-(-65537 // 16)) // 32) * 32
+        splits = -(-65537 // chunk)
+        assert splits == 16
+        q_cat = 16 * 64 * (512 + d_rope) * 2
+        parts = 16 * splits * 64 * (512 * 2 + 2 * 4)
+        assert q_cat + parts <= n <= q_cat + parts + 3 * 256
