@@ -49,7 +49,7 @@ typedef int32_t mla_status;
 #define MLA_E_NULL 1        /* a required pointer is NULL */
 #define MLA_E_SHAPE 2       /* sizes inconsistent with each other */
 #define MLA_E_DTYPE 3       /* unknown dtype code */
-#define MLA_E_UNSUPPORTED 4 /* valid shape that this build has no kernel for */
+#define MLA_E_UNSUPPORTED 4 /* valid shape that the library has no kernel for */
 #define MLA_E_WORKSPACE 5   /* workspace too small */
 #define MLA_E_HIP 6         /* a HIP call or launch failed */
 

@@ -363,7 +363,7 @@ const char* mla_status_string(mla_status s) {
     case MLA_E_NULL: return "a required pointer is NULL";
     case MLA_E_SHAPE: return "inconsistent sizes";
     case MLA_E_DTYPE: return "unknown dtype";
-    case MLA_E_UNSUPPORTED: return "shape not supported by this build";
+    case MLA_E_UNSUPPORTED: return "shape not supported by the library's kernels";
     case MLA_E_WORKSPACE: return "workspace too small";
     case MLA_E_HIP: return "HIP launch failed";
     default: return "unknown status";
