@@ -275,3 +275,100 @@ def draw(w: Workload) -> dict:
         out["x"] = None
         out["w_g"] = None
     return out
+
+
+# --------------------------------------------------------------------------------------
+# Fused append (hidden state -> latent cache row)
+# --------------------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class ProjWorkload:
+    """Shape, layout and seed of one fused latent append: each sequence's n_new new
+    tokens go to positions pos0[b] .. pos0[b] + n_new - 1 of its cache."""
+    name: str
+    dtype: str                 # "f32" or "bf16": hidden state, weights and cache
+    d_model: int
+    d_c: int
+    d_r: int
+    batch: int
+    n_new: int
+    pos0: np.ndarray           # int32 [batch]
+    paged: bool
+    block_size: int = 64
+    pool_blocks: int = 0
+    block_table: Optional[np.ndarray] = None
+    seed: int = 0
+    rope_base: float = 10000.0
+    eps: float = 1e-6
+
+    @property
+    def row(self) -> int:
+        return self.d_c + self.d_r
+
+    @property
+    def rows(self) -> int:
+        return self.batch * self.n_new
+
+    @property
+    def t_max(self) -> int:
+        return int(self.pos0.max()) + self.n_new
+
+    @property
+    def max_blocks(self) -> int:
+        return (self.t_max + self.block_size - 1) // self.block_size
+
+    def positions(self) -> np.ndarray:
+        """Position of every new token, [batch * n_new] in (b, j) order."""
+        return (self.pos0.astype(np.int64)[:, None] + np.arange(self.n_new)[None, :]).reshape(-1)
+
+
+def make_projection(kind: str = "deepseek", batch: Optional[int] = None, n_new: int = 1,
+                    d_model: Optional[int] = None, pos: Optional[int] = None,
+                    pos_range: Optional[tuple] = None, paged: bool = False,
+                    seed: Optional[int] = None) -> ProjWorkload:
+    """A fused-append workload.
+
+    deepseek  bf16, d_model=4096, d_c=512, d_rope=64, B=32, one new token at slot 4096
+              (the decode step of the DeepSeek-shaped workload)
+    nope      bf16, d_model=4096, d_c=512, d_rope=0, B=16 (the position-free variant)
+    tiny      fp32, d_model=24, d_c=32, d_rope=8, B=2 (the tiny layer)
+    Positions are `pos` for every sequence, or uniform in `pos_range` (inclusive).
+    """
+    s = 41006 if seed is None else seed
+    if kind == "deepseek":
+        dt, dm, dc, dr, B = "bf16", 4096, 512, 64, 32
+    elif kind == "nope":
+        dt, dm, dc, dr, B = "bf16", 4096, 512, 0, 16
+    elif kind == "tiny":
+        dt, dm, dc, dr, B = "f32", 24, 32, 8, 2
+    else:
+        raise ValueError("unknown projection workload %r" % kind)
+    B = batch or B
+    dm = d_model or dm
+    if pos_range is not None:
+        pos0 = uniform_int(s, "pos0", B, pos_range[0], pos_range[1])
+    else:
+        pos0 = np.full(B, 4096 if pos is None else pos, np.int32)
+    w = ProjWorkload("append_%s_b%d_n%d_dmodel%d" % (kind, B, n_new, dm), dt, dm, dc, dr, B, n_new,
+                     pos0.astype(np.int32), paged, seed=s)
+    if paged:
+        w.pool_blocks, w.block_table = _paged_table(s, w.pos0 + n_new, w.block_size)
+    return w
+
+
+def draw_projection(w: ProjWorkload) -> dict:
+    """Host tensors of one fused append.
+
+    hidden [B, n_new, d_model]  N(0, 1)
+    w_dkv  [d_model, d_c]       N(0, 1/d_model), so c = h . W_DKV is about N(0, 1)
+    w_kr   [d_model, d_r]       N(0, 1/d_model), or None when d_r == 0
+    gain   [d_c] fp32           1 + N(0, 0.1^2), the RMSNorm gain
+    """
+    s, dt = w.seed, w.dtype
+    std = 1.0 / np.sqrt(w.d_model)
+    return {
+        "hidden": normal(s, "hidden", (w.batch, w.n_new, w.d_model), 1.0, dt),
+        "w_dkv": normal(s, "w_dkv", (w.d_model, w.d_c), std, dt),
+        "w_kr": normal(s, "w_kr", (w.d_model, w.d_r), std, dt) if w.d_r else None,
+        "gain": (1.0 + normal(s, "gain", (w.d_c,), 0.1, "f64")).astype(np.float32),
+    }

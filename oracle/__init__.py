@@ -58,6 +58,11 @@ def _load():
     lib.oracle_round_bf16.argtypes = [ctypes.c_double]
     lib.oracle_cache_keys.restype = None
     lib.oracle_cache_keys.argtypes = [ctypes.POINTER(_Dims), i32, i32, i32, vp, vp, vp]
+    lib.oracle_project_latent.restype = i32
+    lib.oracle_project_latent.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, ctypes.c_double,
+                                          vp, ctypes.c_double, vp]
+    lib.oracle_round_bf16_array.restype = None
+    lib.oracle_round_bf16_array.argtypes = [i64, vp, vp]
     lib.oracle_threads.restype = i32
     lib.oracle_threads.argtypes = []
     _lib = lib
@@ -169,3 +174,44 @@ def unabsorbed_flops(h, d_c, d_n, d_v, d_r, kv_lens, n_q, d_model=0) -> float:
     attn = 2.0 * h * vis * (d_n + d_r + d_v)
     gate = 2.0 * len(kv) * n_q * d_model * h * d_v
     return proj + attn + gate
+
+
+def round_bf16_array(x) -> np.ndarray:
+    """Nearest-even bf16 value of every element (fp64 in, fp64 out)."""
+    x = np.ascontiguousarray(x, np.float64)
+    out = np.empty_like(x)
+    _load().oracle_round_bf16_array(x.size, x.ctypes.data, out.ctypes.data)
+    return out
+
+
+def project_latent(*, hidden, w_dkv, w_kr=None, gain=None, eps: float = 1e-6, pos,
+                   rope_base: float = 10000.0) -> np.ndarray:
+    """Cache rows ``[M, d_c + d_r]`` in fp64 from hidden states: the RMS-normalised
+    down-projection ``gain * c / sqrt(mean(c^2) + eps)`` with ``c = h . W_DKV``,
+    followed by ``RoPE(h . W_KR, pos)``.
+
+    ``hidden [..., d_model]`` (leading dims flattened to M), ``w_dkv [d_model, d_c]``,
+    ``w_kr [d_model, d_r]`` or None, one dtype (float64, float32 or bf16 bits);
+    ``gain [d_c]`` (any float dtype) or None for ones; ``pos`` one position per row.
+    """
+    hidden = np.ascontiguousarray(hidden)
+    t = _type_of(hidden)
+    d_model = hidden.shape[-1]
+    M = hidden.size // d_model if d_model else 0
+    w_dkv = np.ascontiguousarray(w_dkv)
+    d_c = w_dkv.shape[1]
+    d_r = 0 if w_kr is None else np.asarray(w_kr).shape[1]
+    if w_kr is not None:
+        w_kr = np.ascontiguousarray(w_kr)
+    for a in (w_dkv, w_kr):
+        if a is not None and (_type_of(a) != t or a.shape[0] != d_model):
+            raise TypeError("weights must share the hidden state's dtype and d_model")
+    g = None if gain is None else np.ascontiguousarray(gain, np.float64)
+    p = np.ascontiguousarray(np.broadcast_to(np.asarray(pos, np.int64).reshape(-1), (M,)))
+    out = np.full((M, d_c + d_r), np.nan)
+    rc = _load().oracle_project_latent(M, d_model, d_c, d_r, t, hidden.ctypes.data,
+                                       w_dkv.ctypes.data, _ptr(w_kr), _ptr(g), float(eps),
+                                       p.ctypes.data, float(rope_base), out.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle rejected the shapes (odd d_r, d_r > 1024 or eps < 0)")
+    return out

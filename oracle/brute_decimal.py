@@ -110,3 +110,27 @@ def decode(c_kv, k_r, q_nope, q_r, w_uk, w_uv, kv_len: int, h: int, d_c: int, d_
                 row.append(sum(p[t] * V[t][e] for t in range(pos + 1)))
         out.append(row)
     return out
+
+
+def project_latent(hidden, w_dkv, w_kr, gain, eps: float, pos, base: float = 10000.0):
+    """Cache rows from hidden states (tutorial §2.2 and §6.3; interview guide §6.2):
+    [gain * c / sqrt(mean(c^2) + eps) ‖ RoPE(h · W_KR, pos)] with c = h · W_DKV.
+    hidden [M][d_model], w_dkv [d_model][d_c], w_kr [d_model][d_r] (or []), gain
+    [d_c] or None, pos [M], as nested lists of floats. Returns [M][d_c + d_r]."""
+    D = lambda x: Decimal(float(x))
+    d_model = len(hidden[0])
+    d_c = len(w_dkv[0])
+    d_r = len(w_kr[0]) if w_kr else 0
+    base_d = Decimal(float(base))
+    rows = []
+    for m, hrow in enumerate(hidden):
+        h = [D(x) for x in hrow]
+        c = [sum(h[k] * D(w_dkv[k][n]) for k in range(d_model)) for n in range(d_c)]
+        rms = (sum(x * x for x in c) / d_c + D(eps)).sqrt()
+        g = [D(x) for x in gain] if gain is not None else [Decimal(1)] * d_c
+        row = [g[n] * (c[n] / rms) for n in range(d_c)]
+        if d_r:
+            kraw = [sum(h[k] * D(w_kr[k][n]) for k in range(d_model)) for n in range(d_r)]
+            row += _rope(kraw, int(pos[m]), base_d)
+        rows.append(row)
+    return rows

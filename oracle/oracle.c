@@ -309,6 +309,57 @@ void oracle_cache_keys(const oracle_dims* d, int32_t B, int32_t T_stride, int32_
   for (int32_t b = 0; b < B; ++b) rotated_keys(&P, b, kv_len[b], kr + (size_t)b * T_stride * d->d_r);
 }
 
+/*
+ * Latent cache row of one token from its hidden state, for the fused append.
+ * Parity pinned by the tests: 50-digit decimal brute force, torch's rms_norm with
+ * a complex-number RoPE in fp64, the identity-weight closed form, and the gain and
+ * scale invariants.
+ *
+ * Pages: tutorial §2.2 (c_KV = h · W_DKV, W_DKV of d_model × d_c) and §6.3 (an
+ * RMSNorm over the d_c latent right after the down-projection); the interview
+ * guide §6.2 `MLA` module (k_R from its own d_model → d_rope projection of the
+ * same input); linear-algebra page "解耦 RoPE" (k_R is cached rotated).
+ *
+ *   c      = h · W_DKV                                     [d_c]
+ *   c_norm = gain ⊙ c / sqrt(mean_n c[n]² + eps)           (gain NULL: ones)
+ *   k      = RoPE(h · W_KR, pos)                           [d_r]
+ *   out    = [ c_norm ‖ k ] in fp64; the caller rounds to the cache type.
+ *
+ * hidden [M][d_model], w_dkv [d_model][d_c], w_kr [d_model][d_r] of in_type;
+ * gain [d_c] fp64 or NULL; pos [M]; out [M][d_c + d_r]. Returns -1 on a bad shape.
+ */
+int32_t oracle_project_latent(int32_t M, int32_t d_model, int32_t d_c, int32_t d_r,
+                              int32_t in_type, const void* hidden, const void* w_dkv,
+                              const void* w_kr, const double* gain, double eps,
+                              const int64_t* pos, double base, double* out) {
+  if (M < 0 || d_model <= 0 || d_c <= 0 || d_r < 0 || d_r % 2 || d_r > 1024 || !(eps >= 0.0))
+    return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int32_t m = 0; m < M; ++m) {
+    double* row = out + (size_t)m * (d_c + d_r);
+    double kraw[1024];
+    for (int32_t n = 0; n < d_c; ++n) row[n] = 0.0;
+    for (int32_t n = 0; n < d_r; ++n) kraw[n] = 0.0;
+    /* both products, k ascending for every output element */
+    for (int32_t k = 0; k < d_model; ++k) {
+      const double hk = ld(hidden, in_type, (size_t)m * d_model + k);
+      for (int32_t n = 0; n < d_c; ++n) row[n] += hk * ld(w_dkv, in_type, (size_t)k * d_c + n);
+      for (int32_t n = 0; n < d_r; ++n) kraw[n] += hk * ld(w_kr, in_type, (size_t)k * d_r + n);
+    }
+    double ss = 0.0;
+    for (int32_t n = 0; n < d_c; ++n) ss += row[n] * row[n];
+    const double rms = sqrt(ss / (double)d_c + eps);
+    for (int32_t n = 0; n < d_c; ++n) row[n] = (gain ? gain[n] : 1.0) * (row[n] / rms);
+    if (d_r) oracle_rope(kraw, d_r, pos[m], base, row + d_c);
+  }
+  return 0;
+}
+
+/* Storage rounding of n values to bf16 (oracle_round_bf16 elementwise). */
+void oracle_round_bf16_array(int64_t n, const double* x, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_round_bf16(x[i]);
+}
+
 int32_t oracle_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

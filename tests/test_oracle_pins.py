@@ -391,3 +391,87 @@ def test_rejects_undefined_shapes():
         oracle.mla_decode(h=w.h, d_c=w.d_c, d_r=w.d_r, d_n=w.d_n, d_v=w.d_v, c_kv=t["c_kv"],
                           k_r=t["k_r"], kv_lens=[0], q_nope=t["q_nope"], q_r=t["q_r"],
                           w_uk=t["w_uk"], w_uv=t["w_uv"])
+
+
+# ------------------------------------------------------------------ fused append from the hidden state
+
+def run_project(w, t, **kw):
+    return oracle.project_latent(hidden=t["hidden"], w_dkv=t["w_dkv"], w_kr=t["w_kr"],
+                                 gain=kw.pop("gain", t["gain"]), eps=kw.pop("eps", w.eps),
+                                 pos=w.positions(), rope_base=w.rope_base, **kw)
+
+
+def test_round_bf16_array_matches_torch():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal(5000) * 10.0 ** rng.integers(-5, 5, 5000)
+    x[:64] = (np.arange(128, 192) + 0.5) * 2.0 ** -7  # exact ties
+    np.testing.assert_array_equal(oracle.round_bf16_array(x), torch_bf16_round(x))
+
+
+def test_project_latent_matches_50_digit_brute_force():
+    """Every term of the fused append at 50 digits (product, mean square, eps, gain,
+    division, RoPE angle and rotation) on a tiny shape, positions up to 10^4."""
+    from oracle import brute_decimal as dref
+    w = synth.make_projection("tiny", batch=3, n_new=1, pos_range=(0, 10000))
+    t = synth.draw_projection(w)
+    out = run_project(w, t)
+    ref = dref.project_latent(t["hidden"].reshape(w.rows, -1).tolist(), t["w_dkv"].tolist(),
+                              t["w_kr"].tolist(), t["gain"].tolist(), w.eps, w.positions().tolist())
+    ref = np.array([[float(x) for x in row] for row in ref])
+    assert np.max(np.abs(out - ref)) < 1e-13
+
+
+def test_project_latent_matches_torch_rms_norm_and_complex_rope():
+    """torch's own RMSNorm (fp64, CPU) of the numpy product, and RoPE as a complex
+    rotation: an independent implementation of every step, on the DeepSeek dims."""
+    w = synth.make_projection("deepseek", batch=4, n_new=2, pos_range=(0, 40000))
+    t = synth.draw_projection(w)
+    out = run_project(w, t)
+    H = as_f64(t["hidden"]).reshape(w.rows, w.d_model)
+    c = torch.from_numpy(H @ as_f64(t["w_dkv"]))
+    cn = torch.nn.functional.rms_norm(c, (w.d_c,), weight=torch.from_numpy(t["gain"].astype(np.float64)),
+                                      eps=w.eps).numpy()
+    kr = H @ as_f64(t["w_kr"])
+    k = np.stack([rope_complex(kr[m], p) for m, p in enumerate(w.positions())])
+    np.testing.assert_allclose(out[:, :w.d_c], cn, rtol=0, atol=1e-13)
+    # angles up to 4e4 rad carry ~1e-11 of fp64 spacing
+    np.testing.assert_allclose(out[:, w.d_c:], k, rtol=0, atol=1e-10)
+
+
+def test_project_latent_identity_weights_closed_form():
+    """d_model = d_c + d_r with W_DKV = [I; 0] and W_KR = [0; I]: the latent is the
+    hidden state's first d_c values over their RMS, the key is the rest rotated."""
+    d_c, d_r, M = 16, 8, 5
+    rng = np.random.default_rng(5)
+    H = rng.standard_normal((M, d_c + d_r))
+    eye = np.eye(d_c + d_r)
+    pos = np.array([0, 1, 7, 300, 65536])
+    out = oracle.project_latent(hidden=H, w_dkv=eye[:, :d_c], w_kr=eye[:, d_c:], gain=None, eps=0.0,
+                                pos=pos)
+    x = H[:, :d_c]
+    for m in range(M):
+        ratio = out[m, :d_c] / x[m]
+        np.testing.assert_allclose(ratio, ratio[0], rtol=1e-15)
+        assert np.mean(out[m, :d_c] ** 2) == pytest.approx(1.0, rel=1e-15)
+        np.testing.assert_array_equal(out[m, d_c:], oracle.rope(H[m, d_c:], pos[m]))
+    # eps enters under the root: mean square of the result is ms / (ms + eps)
+    eps = 0.25
+    out = oracle.project_latent(hidden=H, w_dkv=eye[:, :d_c], w_kr=None, gain=None, eps=eps, pos=pos)
+    ms = np.mean(x ** 2, axis=1)
+    np.testing.assert_allclose(np.mean(out ** 2, axis=1), ms / (ms + eps), rtol=1e-14)
+
+
+def test_project_latent_gain_and_scale_invariants():
+    """The gain multiplies each latent column; scaling the hidden state leaves the
+    normalised latent unchanged (eps = 0) and scales the key."""
+    w = synth.make_projection("tiny", batch=4, n_new=2, pos_range=(0, 500))
+    t = synth.draw_projection(w)
+    ones = run_project(w, t, gain=None)
+    gained = run_project(w, t)
+    np.testing.assert_allclose(gained[:, :w.d_c], ones[:, :w.d_c] * t["gain"].astype(np.float64),
+                               rtol=1e-15, atol=0)
+    np.testing.assert_array_equal(gained[:, w.d_c:], ones[:, w.d_c:])
+    t4 = dict(t, hidden=(t["hidden"] * np.float32(4.0)))
+    a, b = run_project(w, t, eps=0.0), run_project(w, t4, eps=0.0)
+    np.testing.assert_allclose(b[:, :w.d_c], a[:, :w.d_c], rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(b[:, w.d_c:], 4.0 * a[:, w.d_c:], rtol=1e-14, atol=1e-14)
