@@ -164,6 +164,58 @@ mla_status mla_decode_paged(const mla_dims* dims, const void* pool, const int32_
                             int32_t block_size, int32_t max_blocks, int32_t n_blocks,
                             const mla_decode_args* args, hipStream_t stream);
 
+/*
+ * Fused latent append from the hidden state: the cache row of each new token,
+ *   [ gain ⊙ c / sqrt(mean(c²) + eps)  ‖  RoPE(h · W_KR, pos) ],  c = h · W_DKV,
+ * computed and stored in one call (tutorial §2.2: c_KV = h · W_DKV with W_DKV of
+ * d_model × d_c; §6.3: an RMSNorm over the latent right after the
+ * down-projection; interview guide §6.2 `MLA` module: k_R from its own
+ * d_model → d_rope projection of the same input; linear-algebra page "解耦 RoPE":
+ * k_R is cached rotated). It replaces the caller's projections + normalisation +
+ * mla_append_latent.
+ *
+ * mla_pack_down_weights packs the two projections once into one matrix:
+ *   w_dkv  device [d_model][d_c],    dims->dtype
+ *   w_kr   device [d_model][d_rope], dims->dtype; NULL iff d_rope == 0
+ *   packed device buffer of *packed_bytes bytes owned by the caller, laid out as
+ *          [d_model][d_c + d_rope] (W_DKV's columns, then W_KR's).
+ * With packed == NULL it only writes the needed size (no device access).
+ */
+mla_status mla_pack_down_weights(const mla_dims* dims, int32_t d_model, const void* w_dkv,
+                                 const void* w_kr, void* packed, size_t* packed_bytes,
+                                 hipStream_t stream);
+
+typedef struct {
+  int32_t batch;              /* sequences */
+  int32_t n_new;              /* new tokens per sequence */
+  int32_t d_model;            /* hidden width; bf16: a multiple of 16 */
+  const void* hidden;         /* device [batch][n_new][d_model], dims->dtype */
+  const void* packed_down;    /* device, from mla_pack_down_weights with the same d_model */
+  const float* norm_gain;     /* device [d_c] fp32 RMSNorm gain, or NULL for all ones */
+  float norm_eps;             /* RMSNorm epsilon, >= 0 (added to the mean square) */
+  const int32_t* pos0;        /* device [batch]: position (and slot) of each sequence's first
+                                 new token; token j goes to pos0[b] + j, as in
+                                 mla_append_latent */
+  void* workspace;            /* device scratch, or NULL to query its size */
+  size_t* workspace_bytes;    /* in: size of workspace; out (when workspace == NULL): needed */
+  int32_t k_splits;           /* bf16: 0 lets the library choose; > 0 forces the number of
+                                 d_model splits of the product (d_model must be a multiple
+                                 of 16 * k_splits) */
+} mla_project_args;
+
+/*
+ * Writes the n_new rows per sequence into `cache` (laid out as `layout` says),
+ * exactly where mla_append_latent would. bf16: the products run on the matrix
+ * cores with fp32 accumulation, split over d_model and summed in a fixed order;
+ * normalisation in fp32, RoPE in fp64, one rounding to bf16 per element. fp32:
+ * fp32 products and normalisation. Rows whose position falls outside the layout
+ * (or whose block id is out of range) are skipped. MLA_E_WORKSPACE if
+ * *workspace_bytes is too small; MLA_E_UNSUPPORTED for a bf16 d_model that is not
+ * a multiple of 16 (or of 16 * k_splits).
+ */
+mla_status mla_project_append(const mla_dims* dims, void* cache, const mla_cache_layout* layout,
+                              const mla_project_args* args, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* mla_status_string(mla_status s);
 

@@ -16,7 +16,7 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kTile = 32;       // tokens per attention tile; split ranges are multiples of it
-constexpr int kGateSplit = 16;  // must match the gate kernel
+constexpr int kGateSplit = 16;  // K-splits of the gate logits; must match the combine kernel
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -237,14 +237,15 @@ mla_status decode_impl(const mla_dims* dims, const CacheRef& cache, const mla_de
   if (launch_qprep_bf16(q, stream) != hipSuccess) return MLA_E_HIP;
 
   if (a->gate_x) {
-    GateArgs g{};
+    GemmArgs g{};
     g.x = static_cast<const uint16_t*>(a->gate_x);
-    g.w_g = static_cast<const uint16_t*>(a->w_gate);
+    g.w = static_cast<const uint16_t*>(a->w_gate);
     g.g = reinterpret_cast<float*>(wsb + ws.gate);
     g.M = M;
-    g.d_model = a->d_model;
+    g.K = a->d_model;
     g.N = r.h * 128;
-    if (launch_gate_bf16(g, stream) != hipSuccess) return MLA_E_HIP;
+    g.ksplit = kGateSplit;
+    if (launch_splitk_gemm_bf16(g, stream) != hipSuccess) return MLA_E_HIP;
   }
 
   DecodeArgs d{};
@@ -355,6 +356,95 @@ mla_status mla_decode_paged(const mla_dims* dims, const void* pool, const int32_
   if (args && args->workspace && !block_table) return MLA_E_NULL;
   CacheRef c{pool, block_table, 0, block_size, max_blocks, n_blocks};
   return decode_impl(dims, c, args, stream);
+}
+
+mla_status mla_pack_down_weights(const mla_dims* dims, int32_t d_model, const void* w_dkv, const void* w_kr,
+                                 void* packed, size_t* packed_bytes, hipStream_t stream) {
+  Resolved r;
+  mla_status st = resolve(dims, &r);
+  if (st != MLA_OK) return st;
+  if (!packed_bytes) return MLA_E_NULL;
+  if (d_model <= 0) return MLA_E_SHAPE;
+  const size_t need = static_cast<size_t>(d_model) * (r.d_c + r.d_r) * elem_bytes(r.dtype);
+  if (!packed) {
+    *packed_bytes = need;
+    return MLA_OK;
+  }
+  if (*packed_bytes < need) return MLA_E_WORKSPACE;
+  if (!w_dkv || (r.d_r > 0 && !w_kr)) return MLA_E_NULL;
+  return launch_pack_down(r.dtype == MLA_F32 ? 0 : 1, w_dkv, w_kr, packed, d_model, r.d_c, r.d_r, stream) ==
+                 hipSuccess
+             ? MLA_OK
+             : MLA_E_HIP;
+}
+
+mla_status mla_project_append(const mla_dims* dims, void* cache, const mla_cache_layout* layout,
+                              const mla_project_args* a, hipStream_t stream) {
+  Resolved r;
+  mla_status st = resolve(dims, &r);
+  if (st != MLA_OK) return st;
+  if (!layout || !a || !a->workspace_bytes) return MLA_E_NULL;
+  if (a->batch < 0 || a->n_new < 0 || a->d_model <= 0 || a->k_splits < 0) return MLA_E_SHAPE;
+  if (!(a->norm_eps >= 0.f) || !(a->norm_eps < INFINITY)) return MLA_E_SHAPE;
+  if (layout->block_table) {
+    if (layout->block_size <= 0 || layout->max_blocks <= 0 || layout->n_blocks <= 0) return MLA_E_SHAPE;
+  } else if (layout->t_max <= 0) {
+    return MLA_E_SHAPE;
+  }
+  const int N = r.d_c + r.d_r;
+  const int64_t M = static_cast<int64_t>(a->batch) * a->n_new;
+  if (M > (int64_t(1) << 30)) return MLA_E_UNSUPPORTED;
+  int ks = 1;
+  size_t need = kAlign;
+  if (r.dtype == MLA_BF16) {
+    // split-K product: K in 16s per split, W under 4 GiB (32-bit buffer offsets)
+    if (a->d_model % 16 != 0 || static_cast<int64_t>(a->d_model) * N * 2 >= (int64_t(1) << 32))
+      return MLA_E_UNSUPPORTED;
+    if (a->k_splits > 0) {
+      ks = a->k_splits;
+      if (ks > 1024 || a->d_model % (16 * ks) != 0) return MLA_E_UNSUPPORTED;
+    } else {
+      ks = 32;  // about 160 workgroups for the DeepSeek widths at d_model = 4096
+      while (ks > 1 && a->d_model % (16 * ks) != 0) ks /= 2;
+    }
+    need = std::max(need, align_up(static_cast<size_t>(ks) * M * N * 4));
+  }
+  if (!a->workspace) {
+    *a->workspace_bytes = need;
+    return MLA_OK;
+  }
+  if (*a->workspace_bytes < need) return MLA_E_WORKSPACE;
+  if (M == 0) return MLA_OK;
+  if (!cache || !a->hidden || !a->packed_down || !a->pos0) return MLA_E_NULL;
+
+  ProjArgs p{};
+  p.cache = CacheRef{cache, layout->block_table, layout->t_max, layout->block_size, layout->max_blocks,
+                     layout->n_blocks};
+  p.pos0 = a->pos0;
+  p.hidden = a->hidden;
+  p.w_down = a->packed_down;
+  p.part = static_cast<const float*>(a->workspace);
+  p.gain = a->norm_gain;
+  p.M = static_cast<int32_t>(M);
+  p.n_new = a->n_new;
+  p.d_model = a->d_model;
+  p.d_c = r.d_c;
+  p.d_r = r.d_r;
+  p.ksplit = ks;
+  p.eps = a->norm_eps;
+  p.rope_base = r.rope_base;
+  if (r.dtype == MLA_BF16) {
+    GemmArgs g{};
+    g.x = static_cast<const uint16_t*>(a->hidden);
+    g.w = static_cast<const uint16_t*>(a->packed_down);
+    g.g = static_cast<float*>(a->workspace);
+    g.M = p.M;
+    g.K = a->d_model;
+    g.N = N;
+    g.ksplit = ks;
+    if (launch_splitk_gemm_bf16(g, stream) != hipSuccess) return MLA_E_HIP;
+  }
+  return launch_latent_finish(r.dtype == MLA_F32 ? 0 : 1, p, stream) == hipSuccess ? MLA_OK : MLA_E_HIP;
 }
 
 const char* mla_status_string(mla_status s) {

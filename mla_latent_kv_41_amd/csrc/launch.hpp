@@ -65,13 +65,31 @@ struct CombineArgs {
 };
 hipError_t launch_combine_bf16(const CombineArgs& a, hipStream_t s);
 
-struct GateArgs {
-  const uint16_t* x;    // [M][d_model]
-  const uint16_t* w_g;  // [d_model][N]
-  float* g;             // [M][N] logits
-  int32_t M, d_model, N;
+// g[ks][m][n] = Σ_{k in split ks} x[m][k] w[k][n]; K a multiple of 16 ksplit, N of 32
+struct GemmArgs {
+  const uint16_t* x;  // [M][K]
+  const uint16_t* w;  // [K][N]
+  float* g;           // [ksplit][M][N]
+  int32_t M, K, N, ksplit;
 };
-hipError_t launch_gate_bf16(const GateArgs& a, hipStream_t s);
+hipError_t launch_splitk_gemm_bf16(const GemmArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- fused append
+// Cache row [gain ⊙ RMSNorm(h · W_DKV) ‖ RoPE(h · W_KR, pos)] of each new token.
+hipError_t launch_pack_down(int dtype, const void* w_dkv, const void* w_kr, void* packed, int d_model, int d_c,
+                            int d_r, hipStream_t s);
+struct ProjArgs {
+  CacheRef cache;
+  const int32_t* pos0;   // [batch]: position of each sequence's first new token
+  const void* hidden;    // fp32 path: [M][d_model]
+  const void* w_down;    // fp32 path: packed [d_model][d_c + d_r]
+  const float* part;     // bf16 path: [ksplit][M][d_c + d_r] split partial sums
+  const float* gain;     // [d_c] or nullptr (ones)
+  int32_t M, n_new, d_model, d_c, d_r, ksplit;
+  float eps;
+  double rope_base;
+};
+hipError_t launch_latent_finish(int dtype, const ProjArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- fp32 path
 struct F32Args {

@@ -18,7 +18,7 @@ MLA_OK, MLA_E_NULL, MLA_E_SHAPE, MLA_E_DTYPE, MLA_E_UNSUPPORTED, MLA_E_WORKSPACE
 MLA_F32, MLA_BF16 = 0, 1
 
 EXPORTS = ("mla_absorb_weights", "mla_append_latent", "mla_decode", "mla_decode_paged",
-           "mla_status_string")
+           "mla_pack_down_weights", "mla_project_append", "mla_status_string")
 
 
 class MLAError(RuntimeError):
@@ -51,6 +51,14 @@ class mla_decode_args(ctypes.Structure):
                 ("ev_attn_end", ctypes.c_void_p)]
 
 
+class mla_project_args(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_new", ctypes.c_int32), ("d_model", ctypes.c_int32),
+                ("hidden", ctypes.c_void_p), ("packed_down", ctypes.c_void_p),
+                ("norm_gain", ctypes.c_void_p), ("norm_eps", ctypes.c_float), ("pos0", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.POINTER(ctypes.c_size_t)),
+                ("k_splits", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -76,6 +84,12 @@ def lib():
         L.mla_decode_paged.restype = st
         L.mla_decode_paged.argtypes = [ctypes.POINTER(mla_dims), vp, vp, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.POINTER(mla_decode_args), vp]
+        L.mla_pack_down_weights.restype = st
+        L.mla_pack_down_weights.argtypes = [ctypes.POINTER(mla_dims), ctypes.c_int32, vp, vp, vp,
+                                            ctypes.POINTER(ctypes.c_size_t), vp]
+        L.mla_project_append.restype = st
+        L.mla_project_append.argtypes = [ctypes.POINTER(mla_dims), vp, ctypes.POINTER(mla_cache_layout),
+                                         ctypes.POINTER(mla_project_args), vp]
         L.mla_status_string.restype = ctypes.c_char_p
         L.mla_status_string.argtypes = [ctypes.c_int32]
         _lib = L
@@ -143,6 +157,67 @@ def mla_append_latent(d: mla_dims, cache, *, c_kv, k_r, pos0, t_max: int = 0, bl
     return _check(lib().mla_append_latent(ctypes.byref(d), _ptr(cache), ctypes.byref(layout), B, N,
                                           _ptr(c_kv), _ptr(k_r), _ptr(pos0), _stream(stream)),
                   "mla_append_latent")
+
+
+# ------------------------------------------------------------------------------ fused append
+
+def mla_pack_down_weights(d: mla_dims, d_model: int, w_dkv=None, w_kr=None, packed=None,
+                          packed_bytes=None, stream=None) -> int:
+    """Pack [W_DKV ‖ W_KR] once. With packed=None returns the needed byte count."""
+    n = ctypes.c_size_t(0 if packed_bytes is None else packed_bytes)
+    if packed is None:
+        _check(lib().mla_pack_down_weights(ctypes.byref(d), d_model, None, None, None, ctypes.byref(n),
+                                           None), "mla_pack_down_weights")
+        return n.value
+    if packed_bytes is None:
+        n.value = packed.numel() * packed.element_size()
+    _check(lib().mla_pack_down_weights(ctypes.byref(d), d_model, _ptr(w_dkv), _ptr(w_kr), _ptr(packed),
+                                       ctypes.byref(n), _stream(stream)), "mla_pack_down_weights")
+    return n.value
+
+
+def _project_args(*, batch, n_new, d_model, hidden, packed_down, norm_gain, norm_eps, pos0,
+                  workspace, workspace_bytes, k_splits):
+    nbytes = ctypes.c_size_t(workspace_bytes)
+    a = mla_project_args(batch, n_new, d_model, _ptr(hidden), _ptr(packed_down), _ptr(norm_gain),
+                         norm_eps, _ptr(pos0), _ptr(workspace), ctypes.pointer(nbytes), k_splits)
+    return a, nbytes
+
+
+def mla_project_append(d: mla_dims, cache, *, hidden, packed_down, pos0, norm_gain=None,
+                       norm_eps: float = 1e-6, t_max: int = 0, block_table=None, block_size: int = 0,
+                       max_blocks: int = 0, n_blocks: int = 0, workspace=None, k_splits: int = 0,
+                       d_model: Optional[int] = None, batch: Optional[int] = None,
+                       n_new: Optional[int] = None, stream=None) -> int:
+    """Write [gain * RMSNorm(h . W_DKV) ‖ RoPE(h . W_KR)] rows at positions pos0[b] + j."""
+    B = batch if batch is not None else hidden.shape[0]
+    N = n_new if n_new is not None else hidden.shape[1]
+    D = d_model if d_model is not None else hidden.shape[-1]
+    layout = mla_cache_layout(_ptr(block_table), t_max, block_size, max_blocks, n_blocks)
+    common = dict(batch=B, n_new=N, d_model=D, hidden=hidden, packed_down=packed_down,
+                  norm_gain=norm_gain, norm_eps=norm_eps, pos0=pos0, k_splits=k_splits)
+
+    def query():
+        a, n = _project_args(workspace=None, workspace_bytes=0, **common)
+        _check(lib().mla_project_append(ctypes.byref(d), _ptr(cache), ctypes.byref(layout), ctypes.byref(a),
+                                        None), "mla_project_append")
+        return n.value
+
+    ws = _workspace_for(query, workspace, hidden.device)
+    a, n = _project_args(workspace=ws, workspace_bytes=ws.numel() * ws.element_size(), **common)
+    return _check(lib().mla_project_append(ctypes.byref(d), _ptr(cache), ctypes.byref(layout),
+                                           ctypes.byref(a), _stream(stream)), "mla_project_append")
+
+
+def project_workspace_bytes(d: mla_dims, *, batch: int, n_new: int, d_model: int, k_splits: int = 0) -> int:
+    """Workspace mla_project_append needs (pure host arithmetic; no device access)."""
+    layout = mla_cache_layout(None, 1, 0, 0, 0)
+    a, n = _project_args(batch=batch, n_new=n_new, d_model=d_model, hidden=None, packed_down=None,
+                         norm_gain=None, norm_eps=1e-6, pos0=None, workspace=None, workspace_bytes=0,
+                         k_splits=k_splits)
+    _check(lib().mla_project_append(ctypes.byref(d), None, ctypes.byref(layout), ctypes.byref(a), None),
+           "project_workspace_bytes")
+    return n.value
 
 
 # ------------------------------------------------------------------------------ decode

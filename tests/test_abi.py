@@ -135,3 +135,48 @@ def test_split_plan_64_row_groups():
         q_cat = 16 * 64 * (512 + d_rope) * 2
         parts = 16 * splits * 64 * (512 * 2 + 2 * 4)
         assert q_cat + parts <= n <= q_cat + parts + 3 * 256
+
+
+def call_project(d, *, batch=32, n_new=1, d_model=4096, ws=None, ws_bytes=0, k_splits=0, eps=1e-6,
+                 layout=None):
+    lay = layout or mla.mla_cache_layout(None, 4097, 0, 0, 0)
+    a, n = mla._project_args(batch=batch, n_new=n_new, d_model=d_model, hidden=None, packed_down=None,
+                             norm_gain=None, norm_eps=eps, pos0=None, workspace=ws,
+                             workspace_bytes=ws_bytes, k_splits=k_splits)
+    st = mla.lib().mla_project_append(ctypes.byref(d), None, ctypes.byref(lay), ctypes.byref(a), None)
+    return st, n.value
+
+
+def test_fused_append_sizes_and_rejections():
+    d = ds_dims()
+    assert mla.mla_pack_down_weights(d, 4096) == 4096 * 576 * 2
+    assert mla.mla_pack_down_weights(ds_dims(d_rope=0), 4096) == 4096 * 512 * 2
+    assert mla.mla_pack_down_weights(ds_dims(n_heads=4, d_c=32, d_rope=8, d_qk_nope=16, d_v=16,
+                                             dtype=mla.MLA_F32), 24) == 24 * 40 * 4
+    # the split partials: 32 splits x 32 rows x 576 fp32 by default, or as forced
+    assert call_project(d) == (mla.MLA_OK, 32 * 32 * 576 * 4)
+    assert call_project(d, k_splits=16) == (mla.MLA_OK, 16 * 32 * 576 * 4)
+    assert call_project(d, d_model=4096 + 16)[1] == 32 * 576 * 4  # 4112 = 16 * 257: one split
+    assert call_project(d, d_model=100)[0] == mla.MLA_E_UNSUPPORTED
+    assert call_project(d, k_splits=3)[0] == mla.MLA_E_UNSUPPORTED
+    assert call_project(d, k_splits=-1)[0] == mla.MLA_E_SHAPE
+    assert call_project(d, d_model=0)[0] == mla.MLA_E_SHAPE
+    assert call_project(d, eps=-1.0)[0] == mla.MLA_E_SHAPE
+    assert call_project(d, eps=float("nan"))[0] == mla.MLA_E_SHAPE
+    assert call_project(d, layout=mla.mla_cache_layout(None, 0, 0, 0, 0))[0] == mla.MLA_E_SHAPE
+    assert call_project(d, layout=mla.mla_cache_layout(1, 0, 64, 0, 8))[0] == mla.MLA_E_SHAPE
+    st, n = call_project(d)
+    assert call_project(d, ws=1, ws_bytes=n - 1)[0] == mla.MLA_E_WORKSPACE
+    assert call_project(d, ws=1, ws_bytes=n)[0] == mla.MLA_E_NULL   # no cache / hidden / weights
+    assert call_project(d, batch=0, ws=1, ws_bytes=n)[0] == mla.MLA_OK  # nothing to write
+    lay = mla.mla_cache_layout(None, 16, 0, 0, 0)
+    a, _n = mla._project_args(batch=1, n_new=1, d_model=64, hidden=None, packed_down=None, norm_gain=None,
+                              norm_eps=1e-6, pos0=None, workspace=None, workspace_bytes=0, k_splits=0)
+    assert mla.lib().mla_project_append(ctypes.byref(d), None, ctypes.byref(lay), None, None) == mla.MLA_E_NULL
+    assert mla.lib().mla_project_append(ctypes.byref(d), None, None, ctypes.byref(a), None) == mla.MLA_E_NULL
+    n = ctypes.c_size_t(0)
+    assert mla.lib().mla_pack_down_weights(ctypes.byref(d), 0, None, None, None, ctypes.byref(n), None) == mla.MLA_E_SHAPE
+    n.value = 10
+    assert mla.lib().mla_pack_down_weights(ctypes.byref(d), 64, None, None, 1, ctypes.byref(n), None) == mla.MLA_E_WORKSPACE
+    n.value = 64 * 576 * 2
+    assert mla.lib().mla_pack_down_weights(ctypes.byref(d), 64, None, None, 1, ctypes.byref(n), None) == mla.MLA_E_NULL
