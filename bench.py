@@ -13,6 +13,8 @@ copies of (cache, packed weights) are used in turn, as three layers would be,
 so the 256 MB Infinity Cache cannot hold the working set between steps.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py --config 3|4|5          the other decode workloads
+    python bench.py --workload append       the fused latent append from the hidden state
 """
 from __future__ import annotations
 
@@ -164,6 +166,39 @@ def _bench_line(log_path):
     return json.loads(line)
 
 
+def _short_kernel_name(name):
+    name = name.replace("void ", "", 1)
+    return name.split("(")[0] if not name.startswith("at::") else name.split(")")[0] + ")"
+
+
+def summarize_append_trace(d):
+    """profiles/ summary of a kernel-trace run of the fused-append bench
+    (DIR/prof_append, log DIR/prof_append.log)."""
+    import csv
+    import glob
+    line = _bench_line(os.path.join(d, "prof_append.log"))
+    wl = line["config"]["workload"]
+    stats = list(csv.DictReader(open(glob.glob(os.path.join(d, "prof_append", "*kernel_stats.csv"))[0])))
+    per_call = sum(float(r["AverageNs"]) for r in stats
+                   if "splitk_gemm_kernel" in r["Name"] or "latent_finish_kernel" in r["Name"]) / 1e3
+    lines = ["# Kernel trace: fused latent append, %s (`bench.py --workload append`)" % wl, "",
+             "Command (from /tmp with TMPDIR=/tmp):", "", "    " + APPEND_TRACE_CMD, "",
+             "One call = splitk_gemm_kernel (both projections, split over d_model) then "
+             "latent_finish_kernel (split sum, RMSNorm, RoPE, store). pack_down_kernel and the fills "
+             "belong to set-up.", "",
+             "| kernel | calls | average us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        lines.append("| `%s` | %s | %.2f | %.2f | %.2f | %.1f%% |" % (
+            _short_kernel_name(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    lines += ["", "Sum of the two kernels' averages: %.2f us per call, %.1f GB/s of the %d algorithmic bytes "
+              "per call. (Under the tracer the bench's own clock reads %.2f us per call: the tracer adds "
+              "time to every dispatch.)" % (per_call, line["algorithmic_bytes_per_call"] / (per_call * 1e3),
+                                           line["algorithmic_bytes_per_call"], line["ms_per_step"] * 1e3), ""]
+    open(os.path.join(ROOT, "profiles", "%s_kernel_trace.md" % wl), "w").write("\n".join(lines))
+    print("fused append trace summary written")
+
+
 def summarize_profiles(d):
     """Summaries of a kernel-trace run (DIR/prof_ds, log DIR/prof_ds.log) and of one
     FETCH_SIZE and one WRITE_SIZE counter run (DIR/pmc/<C>, logs DIR/pmc/<C>.log) of
@@ -174,6 +209,10 @@ def summarize_profiles(d):
     import glob
     from collections import defaultdict
     prof = os.path.join(ROOT, "profiles")
+    if os.path.isdir(os.path.join(d, "prof_append")):
+        summarize_append_trace(d)
+    if not os.path.isdir(os.path.join(d, "prof_ds")):
+        return
     w_name = "deepseek_b32_ctx4096"
     kname = "mla::decode_kernel<4, 64>"
     shas = {_bench_line(os.path.join(d, "prof_ds.log"))["attention_kernel_source_sha256"]}
@@ -271,6 +310,123 @@ def summarize_profiles(d):
     print("summaries written for attention kernel source %s" % sha)
 
 
+APPEND_COPIES = 64  # packed down-projection copies, rotated as 64 layers would be
+APPEND_TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out>/prof_append -o append -- "
+                    "python3 bench.py --workload append --steps 400 --warmup 50 --no-cpu-baseline")
+
+
+def append_bytes(w):
+    """Bytes the fused append must move per call: both projections once, the hidden
+    states and the gain in, the new cache rows out."""
+    eb = 4 if w.dtype == "f32" else 2
+    return (w.d_model * w.row * eb + w.rows * w.d_model * eb + w.d_c * 4 + w.batch * 4
+            + w.rows * w.row * eb)
+
+
+def append_cpu_baseline(w, t, budget_s=10.0):
+    """The fp64 oracle of the fused append (as it stands) on the whole workload,
+    repeated for about budget_s, in GB/s of the same algorithmic bytes."""
+    import oracle
+    n, t0 = 0, time.perf_counter()
+    while n == 0 or time.perf_counter() - t0 < budget_s:
+        oracle.project_latent(hidden=t["hidden"], w_dkv=t["w_dkv"], w_kr=t["w_kr"], gain=t["gain"],
+                              eps=w.eps, pos=w.positions(), rope_base=w.rope_base)
+        n += 1
+    secs = time.perf_counter() - t0
+    return {"value": round(append_bytes(w) * n / secs / 1e9, 4), "unit": "GB/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": "the whole workload (%d rows) %d times, fp64 oracle, %.1f s; rows/s %.3g"
+                      % (w.rows, n, secs, w.rows * n / secs)}
+
+
+def bench_append(args):
+    """The fused latent append from the hidden state (mla_project_append) on the
+    DeepSeek-shaped decode step: 32 new tokens, d_model 4096, rows of 512 + 64."""
+    import numpy as np
+    import torch
+    from mla_latent_kv_41_amd import mla, synth
+    from mla_latent_kv_41_amd.harness import to_device
+
+    w = synth.make_projection("deepseek")
+    t = synth.draw_projection(w)
+    log("workload %s: rows=%d d_model=%d row=%d" % (w.name, w.rows, w.d_model, w.row))
+    d = mla.dims(128, w.d_c, w.d_r, 128, 128, mla.MLA_BF16, rope_base=w.rope_base)
+    w_dkv, w_kr = to_device(t["w_dkv"]), to_device(t["w_kr"])
+    nbytes = mla.mla_pack_down_weights(d, w.d_model)
+    packs = []
+    for _ in range(APPEND_COPIES):
+        p = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        mla.mla_pack_down_weights(d, w.d_model, w_dkv, w_kr, p)
+        packs.append(p)
+    hidden, gain = to_device(t["hidden"]), to_device(t["gain"])
+    pos0 = torch.from_numpy(w.pos0.astype(np.int32)).cuda()
+    cache = torch.zeros((w.batch, w.t_max, w.row), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mla.project_workspace_bytes(d, batch=w.batch, n_new=w.n_new, d_model=w.d_model,
+                                                 k_splits=args.k_splits), dtype=torch.uint8, device="cuda")
+
+    # arguments marshalled once per weight copy: a Python-built call per step would
+    # take longer than the GPU work it launches
+    calls = [mla.prepare_project_append(d, cache, hidden=hidden, packed_down=p, pos0=pos0, workspace=ws,
+                                        norm_gain=gain, norm_eps=w.eps, t_max=w.t_max,
+                                        k_splits=args.k_splits) for p in packs]
+
+    def call(k):
+        calls[k % APPEND_COPIES]()
+
+    t0 = time.perf_counter()
+    k = 0
+    while time.perf_counter() - t0 < SETTLE_S:
+        for _ in range(256):
+            call(k)
+            k += 1
+        torch.cuda.synchronize()
+    for k in range(args.warmup):
+        call(k)
+    torch.cuda.synchronize()
+    # HIP events (torch's, on torch's current stream, where the library launches)
+    # around the K timed calls; the per-call average is the roofline figure. It
+    # spans both kernels of a call and the gap between them.
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for k in range(args.steps):
+        call(k)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    alg = append_bytes(w)
+    gbps = alg / (ms * 1e-3) / 1e9
+    flops = 2.0 * w.rows * w.d_model * w.row
+    out = {
+        "metric": "fused latent append GB/s (% of HBM peak), 32 new tokens, d_model=4096, row 512+64",
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; N(0,1) hidden states, N(0,1/d_model) weights, gain 1+N(0,0.01))",
+        "config": {"workload": w.name, "batch": w.batch, "new_tokens": w.n_new, "d_model": w.d_model,
+                   "d_c": w.d_c, "d_rope": w.d_r, "position": int(w.pos0[0]),
+                   "cache": "contiguous bf16 [%d, %d, %d]" % (w.batch, w.t_max, w.row),
+                   "weight_copies_rotated": APPEND_COPIES,
+                   "k_splits": args.k_splits or "library's choice"},
+        "algorithmic_bytes_per_call": alg,
+        "tflops": round(flops / (ms * 1e-3) / 1e12, 3),
+        "rows_per_s": round(w.rows / (ms * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "one mla_project_append call: splitk_gemm_kernel then latent_finish_kernel",
+                     "algorithmic_bytes_per_launch": alg},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = append_cpu_baseline(w, t)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -282,6 +438,11 @@ def main():
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5],
                     help="workload: 2 DeepSeek-shaped (default, the headline), 3 paged long "
                          "context, 4 ragged with two queries, 5 gated h=64 without RoPE")
+    ap.add_argument("--workload", default="decode", choices=["decode", "append"],
+                    help="decode: the decode step (default); append: the fused latent append "
+                         "from the hidden state (mla_project_append)")
+    ap.add_argument("--k-splits", type=int, default=0,
+                    help="append workload: force the d_model splits of the product (0: library)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write profiles/ summaries from rocprofv3 output under DIR "
                          "(no GPU work)")
@@ -293,6 +454,9 @@ def main():
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "append":
+        bench_append(args)
+        return
 
     import numpy as np
     import torch

@@ -207,8 +207,9 @@ typedef struct {
  * Writes the n_new rows per sequence into `cache` (laid out as `layout` says),
  * exactly where mla_append_latent would. bf16: the products run on the matrix
  * cores with fp32 accumulation, split over d_model and summed in a fixed order;
- * normalisation in fp32, RoPE in fp64, one rounding to bf16 per element. fp32:
- * fp32 products and normalisation. Rows whose position falls outside the layout
+ * normalisation in fp32; RoPE angles formed and reduced modulo 2π in fp64, their
+ * sine, cosine and the rotation in fp32; one rounding to bf16 per element. fp32:
+ * the same in fp32 arithmetic, without the matrix cores. Rows whose position falls outside the layout
  * (or whose block id is out of range) are skipped. MLA_E_WORKSPACE if
  * *workspace_bytes is too small; MLA_E_UNSUPPORTED for a bf16 d_model that is not
  * a multiple of 16 (or of 16 * k_splits).

@@ -432,7 +432,7 @@ mla_status mla_project_append(const mla_dims* dims, void* cache, const mla_cache
   p.d_r = r.d_r;
   p.ksplit = ks;
   p.eps = a->norm_eps;
-  p.rope_base = r.rope_base;
+  for (int k = 0; k < r.d_r / 2 && k < kMaxRopePairs; ++k) p.inv_freq[k] = pow(r.rope_base, -2.0 * k / r.d_r);
   if (r.dtype == MLA_BF16) {
     GemmArgs g{};
     g.x = static_cast<const uint16_t*>(a->hidden);

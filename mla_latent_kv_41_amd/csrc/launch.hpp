@@ -76,6 +76,7 @@ hipError_t launch_splitk_gemm_bf16(const GemmArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- fused append
 // Cache row [gain ⊙ RMSNorm(h · W_DKV) ‖ RoPE(h · W_KR, pos)] of each new token.
+constexpr int kMaxRopePairs = 128;  // d_r <= 256
 hipError_t launch_pack_down(int dtype, const void* w_dkv, const void* w_kr, void* packed, int d_model, int d_c,
                             int d_r, hipStream_t s);
 struct ProjArgs {
@@ -87,7 +88,7 @@ struct ProjArgs {
   const float* gain;     // [d_c] or nullptr (ones)
   int32_t M, n_new, d_model, d_c, d_r, ksplit;
   float eps;
-  double rope_base;
+  double inv_freq[kMaxRopePairs];  // rope_base^(-2k/d_r), computed on the host in fp64
 };
 hipError_t launch_latent_finish(int dtype, const ProjArgs& a, hipStream_t s);
 

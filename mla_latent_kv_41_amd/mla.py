@@ -209,6 +209,28 @@ def mla_project_append(d: mla_dims, cache, *, hidden, packed_down, pos0, norm_ga
                                            ctypes.byref(a), _stream(stream)), "mla_project_append")
 
 
+def prepare_project_append(d: mla_dims, cache, *, hidden, packed_down, pos0, workspace, norm_gain=None,
+                           norm_eps: float = 1e-6, t_max: int = 0, block_table=None, block_size: int = 0,
+                           max_blocks: int = 0, n_blocks: int = 0, k_splits: int = 0, stream=None):
+    """mla_project_append with its arguments marshalled once: returns a function of
+    no arguments that makes the same call (for loops where Python's per-call
+    argument building would outlast the GPU work). The tensors must stay alive."""
+    B, N, D = hidden.shape[0], hidden.shape[1], hidden.shape[-1]
+    layout = mla_cache_layout(_ptr(block_table), t_max, block_size, max_blocks, n_blocks)
+    a, n = _project_args(batch=B, n_new=N, d_model=D, hidden=hidden, packed_down=packed_down,
+                         norm_gain=norm_gain, norm_eps=norm_eps, pos0=pos0, workspace=workspace,
+                         workspace_bytes=workspace.numel() * workspace.element_size(), k_splits=k_splits)
+    fn, dref, cref, lref, aref = (lib().mla_project_append, ctypes.byref(d), _ptr(cache),
+                                  ctypes.byref(layout), ctypes.byref(a))
+    st = _stream(stream)
+    keep = (d, layout, a, n)
+
+    def call():
+        _ = keep
+        return _check(fn(dref, cref, lref, aref, st), "mla_project_append")
+    return call
+
+
 def project_workspace_bytes(d: mla_dims, *, batch: int, n_new: int, d_model: int, k_splits: int = 0) -> int:
     """Workspace mla_project_append needs (pure host arithmetic; no device access)."""
     layout = mla_cache_layout(None, 1, 0, 0, 0)

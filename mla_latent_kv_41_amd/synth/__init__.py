@@ -349,7 +349,7 @@ def make_projection(kind: str = "deepseek", batch: Optional[int] = None, n_new: 
         pos0 = uniform_int(s, "pos0", B, pos_range[0], pos_range[1])
     else:
         pos0 = np.full(B, 4096 if pos is None else pos, np.int32)
-    w = ProjWorkload("append_%s_b%d_n%d_dmodel%d" % (kind, B, n_new, dm), dt, dm, dc, dr, B, n_new,
+    w = ProjWorkload("fused_append_%s_b%d_n%d_dmodel%d" % (kind, B, n_new, dm), dt, dm, dc, dr, B, n_new,
                      pos0.astype(np.int32), paged, seed=s)
     if paged:
         w.pool_blocks, w.block_table = _paged_table(s, w.pos0 + n_new, w.block_size)
