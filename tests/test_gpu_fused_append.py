@@ -157,10 +157,12 @@ def test_fused_append_without_rope():
     check_bf16_rows(w, cache, oracle_rows(w, t), "nope")
 
 
-@pytest.mark.parametrize("d_model,k_splits", [(2048, 0), (4096 + 16, 0), (1024, 1), (4096, 4), (4096, 16)])
+@pytest.mark.parametrize("d_model,k_splits", [(2048, 0), (4096 + 16, 0), (1024, 1), (4096, 4), (4096, 16),
+                                               (16384, 0)])
 def test_fused_append_widths_and_splits(d_model, k_splits):
     """Other widths and forced split counts (one split with a 16-row tail chunk
-    at 4112; 4, 16 and the default 32 at 4096): all within 1 ulp of the oracle."""
+    at 4112; 4, 16 and the default 32 at 4096; 512-row splits at 16384): all
+    within the bound."""
     w = synth.make_projection("deepseek", batch=5, n_new=2, d_model=d_model, pos_range=(0, 500))
     t = synth.draw_projection(w)
     say("fused append d_model=%d k_splits=%d" % (d_model, k_splits))
@@ -224,3 +226,52 @@ def test_fused_append_feeds_the_decode():
     rms = float(np.sqrt(np.mean(ref * ref)))
     say("  decode over fused rows: max-abs %.3e, rms %.3e" % (err, rms))
     assert err <= 2e-2 * rms
+
+
+def test_fused_append_skips_rows_outside_the_cache():
+    """Rows whose position is negative or past the cache, or whose block-table entry
+    is -1 or past the pool, are skipped: the kernels' own range checks, no access
+    outside the buffers. Every other row is written as usual."""
+    say("fused append out-of-range rows")
+    # contiguous: t_max = 64; sequence 1 starts at 63 (its second token falls off the
+    # end), sequence 2 at -1 (its first token is skipped), sequence 3 far past the end
+    w = synth.make_projection("deepseek", batch=4, n_new=2, pos=0)
+    w.pos0 = np.array([10, 63, -1, 500], np.int32)
+    t = synth.draw_projection(w)
+    ref = oracle.round_bf16_array(oracle_rows(w, t))
+    d = mla.dims(128, w.d_c, w.d_r, 128, 128, mla.MLA_BF16)
+    packed = torch.empty(mla.mla_pack_down_weights(d, w.d_model), dtype=torch.uint8, device="cuda")
+    mla.mla_pack_down_weights(d, w.d_model, to_device(t["w_dkv"]), to_device(t["w_kr"]), packed)
+    cache = torch.full((4, 64, w.row), float("nan"), dtype=torch.bfloat16, device="cuda")
+    mla.mla_project_append(d, cache, hidden=to_device(t["hidden"]), packed_down=packed,
+                           pos0=torch.from_numpy(w.pos0).cuda(), norm_gain=to_device(t["gain"]),
+                           norm_eps=w.eps, t_max=64)
+    torch.cuda.synchronize()
+    written = {(0, 10): 0, (0, 11): 1, (1, 63): 2, (2, 0): 5}   # (b, slot) -> oracle row
+    flat = cache.float().cpu().numpy()
+    for b in range(4):
+        for s_ in range(64):
+            if (b, s_) in written:
+                got = synth.bf16_bits_to_f64(bf16_bits(cache[b, s_]))
+                np.testing.assert_allclose(got, ref[written[(b, s_)]], rtol=0.0079, atol=1e-4)
+            else:
+                assert np.isnan(flat[b, s_]).all(), (b, s_)
+    # paged: table rows with a -1 entry and an id past the pool
+    wp = synth.make_projection("deepseek", batch=3, n_new=1, pos=0, paged=True)
+    wp.pos0 = np.array([5, 70, 130], np.int32)
+    pool_blocks = 4
+    table = np.array([[1, 2, 0], [3, -1, 0], [2, 0, 9]], np.int32)  # seq 1 -> -1, seq 2 -> 9 >= pool
+    tp = synth.draw_projection(wp)
+    refp = oracle.round_bf16_array(oracle_rows(wp, tp))
+    pool = torch.full((pool_blocks, 64, wp.row), float("nan"), dtype=torch.bfloat16, device="cuda")
+    mla.mla_project_append(d, pool, hidden=to_device(tp["hidden"]), packed_down=packed,
+                           pos0=torch.from_numpy(wp.pos0).cuda(), norm_gain=to_device(tp["gain"]),
+                           norm_eps=wp.eps, block_table=torch.from_numpy(table).cuda(), block_size=64,
+                           max_blocks=3, n_blocks=pool_blocks)
+    torch.cuda.synchronize()
+    got = synth.bf16_bits_to_f64(bf16_bits(pool[1, 5]))
+    np.testing.assert_allclose(got, refp[0], rtol=0.0079, atol=1e-4)
+    rest = pool.float().reshape(-1, wp.row)
+    keep = torch.ones(rest.shape[0], dtype=torch.bool)
+    keep[1 * 64 + 5] = False
+    assert bool(torch.isnan(rest[keep.cuda()]).all())
