@@ -420,6 +420,7 @@ mla_status mla_project_append(const mla_dims* dims, void* cache, const mla_cache
   ProjArgs p{};
   p.cache = CacheRef{cache, layout->block_table, layout->t_max, layout->block_size, layout->max_blocks,
                      layout->n_blocks};
+  p.cache_out = cache;
   p.pos0 = a->pos0;
   p.hidden = a->hidden;
   p.w_down = a->packed_down;

@@ -80,7 +80,8 @@ constexpr int kMaxRopePairs = 128;  // d_r <= 256
 hipError_t launch_pack_down(int dtype, const void* w_dkv, const void* w_kr, void* packed, int d_model, int d_c,
                             int d_r, hipStream_t s);
 struct ProjArgs {
-  CacheRef cache;
+  CacheRef cache;        // addressing of the destination (its data pointer is not written through)
+  void* cache_out;       // the cache itself, written
   const int32_t* pos0;   // [batch]: position of each sequence's first new token
   const void* hidden;    // fp32 path: [M][d_model]
   const void* w_down;    // fp32 path: packed [d_model][d_c + d_r]

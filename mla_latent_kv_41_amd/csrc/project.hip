@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kFinishThreads) void latent_finish_kernel(ProjArgs 
   const float inv = 1.0f / sqrtf(total / static_cast<float>(a.d_c) + a.eps);
 
   if (slot < 0) return;  // uniform per workgroup
-  T* dst = static_cast<T*>(const_cast<void*>(c.data)) + slot * N;
+  T* dst = static_cast<T*>(a.cache_out) + slot * N;
 
 #pragma unroll
   for (int q = 0; q <= kMaxRow / kFinishThreads; ++q) {
