@@ -199,6 +199,72 @@ def summarize_append_trace(d):
     print("fused append trace summary written")
 
 
+def _counter_table(d, sub):
+    """{(kernel, grid): {counter: [values]}} of the FETCH_SIZE and WRITE_SIZE runs
+    under DIR/sub, and the calibration factors from the 512 MiB copy."""
+    import csv
+    import glob
+    from collections import defaultdict
+    vals = defaultdict(lambda: defaultdict(list))
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        for f in glob.glob(os.path.join(d, sub, c, "*counter_collection.csv")):
+            for r in csv.DictReader(open(f)):
+                vals[(_short_kernel_name(r["Kernel_Name"]), int(r["Grid_Size"]))][r["Counter_Name"]].append(
+                    float(r["Counter_Value"]))
+    copy = [k for k in vals if "copyBuffer" in k[0] and k[1] == COPY_BYTES // 4096]
+    if len(copy) != 1:
+        raise SystemExit("calibration copy not found in the counter runs under %s" % sub)
+    cf = {c: sum(v) / len(v) for c, v in vals[copy[0]].items()}
+    return vals, cf, COPY_BYTES / (cf["FETCH_SIZE"] * 1024), COPY_BYTES / (cf["WRITE_SIZE"] * 1024)
+
+
+def summarize_append_counters(d):
+    """profiles/ counter summary and append_traffic.json from one FETCH_SIZE and one
+    WRITE_SIZE run of the fused-append bench (DIR/pmc_append/<C>, logs <C>.log)."""
+    shas = {_bench_line(os.path.join(d, "pmc_append", c + ".log"))["append_kernel_source_sha256"]
+            for c in ("FETCH_SIZE", "WRITE_SIZE")}
+    if len(shas) != 1:
+        raise SystemExit("counter runs used different fused-append sources: %s" % shas)
+    sha = shas.pop()
+    line = _bench_line(os.path.join(d, "pmc_append", "FETCH_SIZE.log"))
+    wl = line["config"]["workload"]
+    vals, cf, f_fac, w_fac = _counter_table(d, "pmc_append")
+    per = {}
+    for name in ("mla::splitk_gemm_kernel", "mla::latent_finish_kernel<unsigned short>"):
+        ks = [k for k in vals if k[0] == name]
+        if len(ks) != 1:
+            raise SystemExit("%s not found once in the counter runs" % name)
+        v = {c: sum(x) / len(x) for c, x in vals[ks[0]].items()}
+        per[name] = (ks[0][1], len(vals[ks[0]]["FETCH_SIZE"]), v["FETCH_SIZE"], v["WRITE_SIZE"],
+                     v["FETCH_SIZE"] * 1024 * f_fac, v["WRITE_SIZE"] * 1024 * w_fac)
+    total = sum(p[4] + p[5] for p in per.values())
+    lines = ["# HBM traffic counters: fused latent append, %s" % wl, "",
+             "Commands (one counter per pass, from /tmp with TMPDIR=/tmp; `--calibrate-copy` adds one 512 MiB "
+             "device-to-device copy):", ""]
+    lines += ["    " + APPEND_PMC_CMD.format(c=c) for c in ("FETCH_SIZE", "WRITE_SIZE")]
+    lines += ["", "Summarised with `python3 bench.py --summarize-profiles <out>`. Fused-append source sha256 "
+              "(%s): `%s`" % (" + ".join("mla_latent_kv_41_amd/csrc/" + f for f in APPEND_SOURCES), sha), "",
+              "| kernel | grid | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | fetch MB | write MB |",
+              "|---|---|---|---|---|---|---|"]
+    for n, p in per.items():
+        lines.append("| `%s` | %d | %d | %.1f | %.1f | %.3f | %.3f |" % (n, p[0], p[1], p[2], p[3], p[4] / 1e6,
+                                                                     p[5] / 1e6))
+    lines += ["", "Calibration: the 512 MiB copy counts FETCH_SIZE %.1f KiB (factor %.4f) and WRITE_SIZE %.1f KiB "
+              "(factor %.4f)." % (cf["FETCH_SIZE"], f_fac, cf["WRITE_SIZE"], w_fac), "",
+              "Per call (both kernels): %.3f MB, against %d algorithmic bytes (the weights once, the hidden "
+              "states, the gain, the rows written). The difference is the split partial sums, written by "
+              "the product and read back by the finishing kernel." % (total / 1e6,
+                                                                       line["algorithmic_bytes_per_call"]), ""]
+    open(os.path.join(ROOT, "profiles", "%s_hbm_counters.md" % wl), "w").write("\n".join(lines))
+    rec = {"kernels": list(per), "workload": wl, "kernel_source_sha256": sha,
+           "kernel_sources": ["mla_latent_kv_41_amd/csrc/" + f for f in APPEND_SOURCES],
+           "copy_calibration": {"fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4)},
+           "bytes_per_kernel": {n: int(p[4] + p[5]) for n, p in per.items()},
+           "bytes_per_call": int(total)}
+    json.dump(rec, open(os.path.join(ROOT, "profiles", "append_traffic.json"), "w"), indent=1)
+    print("fused append counter summary written")
+
+
 def summarize_profiles(d):
     """Summaries of a kernel-trace run (DIR/prof_ds, log DIR/prof_ds.log) and of one
     FETCH_SIZE and one WRITE_SIZE counter run (DIR/pmc/<C>, logs DIR/pmc/<C>.log) of
@@ -211,6 +277,8 @@ def summarize_profiles(d):
     prof = os.path.join(ROOT, "profiles")
     if os.path.isdir(os.path.join(d, "prof_append")):
         summarize_append_trace(d)
+    if os.path.isdir(os.path.join(d, "pmc_append")):
+        summarize_append_counters(d)
     if not os.path.isdir(os.path.join(d, "prof_ds")):
         return
     w_name = "deepseek_b32_ctx4096"
@@ -313,6 +381,26 @@ def summarize_profiles(d):
 APPEND_COPIES = 64  # packed down-projection copies, rotated as 64 layers would be
 APPEND_TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out>/prof_append -o append -- "
                     "python3 bench.py --workload append --steps 400 --warmup 50 --no-cpu-baseline")
+APPEND_PMC_CMD = ("rocprofv3 --pmc {c} --output-format csv -d <out>/pmc_append/{c} -o {c} -- "
+                  "python3 bench.py --workload append --steps 20 --warmup 5 --no-cpu-baseline --calibrate-copy")
+APPEND_SOURCES = ("gemm_bf16.hip", "project.hip", "common.hpp")  # the fused append's kernels
+
+
+def append_source_hash():
+    h = hashlib.sha256()
+    for f in APPEND_SOURCES:
+        h.update(open(os.path.join(ROOT, "mla_latent_kv_41_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def append_traffic_from_profile():
+    """HBM bytes per fused-append call (both kernels) from the committed counter
+    runs, or None when absent or taken on different kernel sources."""
+    p = os.path.join(ROOT, "profiles", "append_traffic.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    return d.get("bytes_per_call") if d.get("kernel_source_sha256") == append_source_hash() else None
 
 
 def append_bytes(w):
@@ -363,6 +451,12 @@ def bench_append(args):
     cache = torch.zeros((w.batch, w.t_max, w.row), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(mla.project_workspace_bytes(d, batch=w.batch, n_new=w.n_new, d_model=w.d_model,
                                                  k_splits=args.k_splits), dtype=torch.uint8, device="cuda")
+    if args.calibrate_copy:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # arguments marshalled once per weight copy: a Python-built call per step would
     # take longer than the GPU work it launches
@@ -417,8 +511,9 @@ def bench_append(args):
         "algorithmic_bytes_per_call": alg,
         "tflops": round(flops / (ms * 1e-3) / 1e12, 3),
         "rows_per_s": round(w.rows / (ms * 1e-3), 1),
+        "append_kernel_source_sha256": append_source_hash(),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": append_traffic_from_profile(),
                      "kernel": "one mla_project_append call: splitk_gemm_kernel then latent_finish_kernel",
                      "algorithmic_bytes_per_launch": alg},
     }
