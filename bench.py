@@ -125,6 +125,30 @@ def traffic_from_profile(per_launch_units):
     return d.get("bytes_per_launch")
 
 
+def stream_read_gbps(nbytes=1 << 30, reps=10):
+    """A secondary reference, never a roofline denominator: HBM read bandwidth of a
+    plain stream on this GPU, measured outside the timed region as torch's row sums
+    of an fp32 [nbytes / 16 KiB, 4096] matrix (it reads nbytes and writes 1/4096 of
+    that; the fastest plain read among torch's reductions and GEMVs measured here),
+    median of reps after warm-up."""
+    import numpy as np
+    import torch
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda").view(-1, 4096)
+    for _ in range(3):
+        x.sum(1)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        x.sum(1)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    del x
+    return round(nbytes / (float(np.median(times)) * 1e-3) / 1e9, 1)
+
+
 def cpu_baseline(w, t, budget_s=12.0):
     """The fp64 oracle (explicit K/V, as it stands) on whole sequences of the same
     workload until about budget_s of CPU time, scaled to TFLOP/s of the absorbed
@@ -656,6 +680,9 @@ def main():
         "attention_kernel_source_sha256": kernel_source_hash(),
         "roofline": roof,
     }
+    if not args.no_cpu_baseline:
+        out["stream_read_GBps"] = stream_read_gbps()
+        out["attention_frac_of_stream_read"] = round(attn_gbps / out["stream_read_GBps"], 4)
     if not args.no_cpu_baseline and args.config == 2:
         out["cpu_baseline"] = cpu_baseline(w, t)
     print(json.dumps(out), flush=True)
