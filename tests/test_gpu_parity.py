@@ -235,6 +235,30 @@ def test_64_row_groups_with_rope(cid, h, batch):
     assert np.max(np.abs(step.lse.cpu().numpy() - lse)) <= 1e-2
 
 
+@pytest.mark.parametrize("cid,n_q", [(2, 4), (4, 4), (4, 8), (5, 4)])
+def test_several_new_tokens_per_sequence(cid, n_q):
+    """4 or 8 new tokens per sequence (a draft of speculative decoding, say): query j
+    sits at kv_len - n_q + j and sees no later new token. 128-row workgroups hold
+    128 / n_q heads x n_q queries. Contiguous, paged ragged, and the gated shape
+    without RoPE, at 1.5-2.5K tokens: every output against 2e-2 x RMS and, without
+    the gate, every output against the first-order bound of its bf16 roundings; lse."""
+    w = synth.make_workload(cid, batch=2, ctx=2000) if cid != 4 else \
+        synth.make_workload(cid, batch=2, ctx_range=(1500, 2500))
+    w.n_q = n_q                       # same lengths: the last n_q tokens are the new ones
+    say("case %d h=%d B=%d n_q=%d kv=[%d..%d]" % (cid, w.h, w.batch, w.n_q, w.kv_lens.min(), w.kv_lens.max()))
+    t = synth.draw(w)
+    step = GpuStep(w, t)
+    out = step.decode().cpu().numpy().astype(np.float64)
+    ref, lse = oracle_out(w, t, want_lse=True)
+    check_bf16(out, ref, what="case %d n_q=%d" % (cid, n_q))
+    if not w.gated:
+        err = np.abs(out - ref)
+        bound = bf16_error_bound(w, t)
+        say("  max err/bound %.3f" % float(np.max(err / bound)))
+        assert np.max(err / bound) <= 1.0
+    assert np.max(np.abs(step.lse.cpu().numpy() - lse)) <= 1e-2
+
+
 def test_split_count_does_not_change_the_result():
     w = synth.make_workload(2, batch=2, ctx=2000)
     t = synth.draw(w)
