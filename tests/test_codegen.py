@@ -45,7 +45,7 @@ PACKED_F32 = re.compile(r"^v_pk_(add|mul|fma)_f32")
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipcc") is None, reason="hipcc not found")
-@pytest.mark.parametrize("name", ["decode_bf16", "combine_bf16", "prep_bf16", "append", "f32_path"])
+@pytest.mark.parametrize("name", sorted(os.path.basename(p)[:-4] for p in build.sources()))
 def test_device_code_properties(name):
     asm = device_asm(os.path.join(build.CSRC, name + ".hip"))
     insts = list(instructions(asm))
