@@ -63,3 +63,29 @@ def test_device_code_properties(name):
         if mnem.startswith("buffer_load") and s.endswith(" lds"):
             prev = [t for t in insts[max(0, k - 3):k] if "m0" in t]
             assert prev, ("direct-to-LDS load without its M0 write", s)
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipcc") is None, reason="hipcc not found")
+@pytest.mark.parametrize("name", sorted(os.path.basename(p)[:-4] for p in build.sources()))
+def test_kernels_use_no_scratch(name):
+    """No kernel spills vector registers or uses scratch memory (SGPR spills go to
+    VGPR lanes and are allowed). Each kernel's metadata map lists its keys in
+    alphabetical order, .name among them, so a map is read as one block."""
+    asm = device_asm(os.path.join(build.CSRC, name + ".hip"))
+    meta = asm[asm.find("amdhsa.kernels:"):]
+    blocks = re.split(r"\n\s+- \.", meta)
+    kernels = {}
+    for b in blocks:
+        nm = re.search(r"(?:^|\n)\s*\.?name:\s+(_Z\S+)", "." + b)
+        if not nm:
+            continue
+        vals = dict((k, int(v)) for k, v in re.findall(
+            r"\.?(private_segment_fixed_size|vgpr_spill_count):\s+(\d+)", "." + b))
+        kernels[nm.group(1)] = vals
+    if name == "api":
+        return  # host code only
+    assert kernels, "no kernel metadata parsed"
+    for k, v in kernels.items():
+        assert set(v) == {"private_segment_fixed_size", "vgpr_spill_count"}, (k, v)  # both parsed
+        assert v["private_segment_fixed_size"] == 0, (k, v)
+        assert v["vgpr_spill_count"] == 0, (k, v)
