@@ -7,6 +7,7 @@ device assembly without a GPU).
 - No scalar-cache writes (scalar stores, scalar atomics, write-back of that cache).
 - No packed fp32 VALU instructions (the build disables their formation).
 """
+import functools
 import os
 import re
 import shutil
@@ -19,6 +20,7 @@ from mla_latent_kv_41_amd import build
 HIPCC = build.HIPCC
 
 
+@functools.lru_cache(maxsize=None)
 def device_asm(src):
     flags = [f for f in build.FLAGS if f not in ("-fPIC", "-shared")]
     res = subprocess.run([HIPCC, *flags, "--cuda-device-only", "-S", src, "-o", "-"],
