@@ -83,8 +83,11 @@ Plan plan_bf16(const Resolved& r, const mla_decode_args* a) {
     int64_t total = 0;
     for (int b = 0; b < a->batch; ++b) total += std::min(a->kv_lens_host[b], L);
     if (total * 5 < static_cast<int64_t>(a->batch) * L * 4) {
-      // ragged batch: ranges sized so the batch yields about two workgroups per slot
-      const int64_t per_wg = std::max<int64_t>(kTile, (total * p.hgroups + 2 * target - 1) / (2 * target));
+      // ragged batch: ranges sized so the batch yields about three workgroups per slot
+      // (measured on the ragged two-query workload: 1, 2, 3, 4 per slot give an
+      // attention kernel of 370, 332, 323, 335 us; more ranges balance the lengths
+      // better until the combine's extra partial rows outweigh it)
+      const int64_t per_wg = std::max<int64_t>(kTile, (total * p.hgroups + 3 * target - 1) / (3 * target));
       split_target = std::max<int64_t>(1, (L + per_wg - 1) / per_wg);
     }
   }
