@@ -277,8 +277,14 @@ def test_split_count_does_not_change_the_result():
         assert d <= BF16_TOL * rms
 
 
-def test_paged_equals_contiguous_bitwise():
+@pytest.mark.parametrize("block_size", [32, 64, 128, 256])
+def test_paged_equals_contiguous_bitwise(block_size):
+    """Any block size that is a multiple of the 32-token tile: each tile is looked up
+    in the block table on its own, so the result does not depend on the layout."""
     w = synth.make_workload(3, batch=2, ctx=1500)
+    w.block_size = block_size
+    w.pool_blocks, w.block_table = synth._paged_table(w.seed, w.kv_lens, block_size)
+    say("paged block_size %d: pool %d blocks" % (block_size, w.pool_blocks))
     t = synth.draw(w)
     paged = GpuStep(w, t).decode().cpu().numpy()
     wc = synth.make_workload(3, batch=2, ctx=1500)
