@@ -51,72 +51,89 @@ mla_status resolve(const mla_dims* d, Resolved* r) {
 size_t elem_bytes(int dtype) { return dtype == MLA_F32 ? 4 : 2; }
 
 // Split plan for the bf16 path.
+//
+// Sequences shorter than kPreciseBelow tokens take the precise attention form (query
+// and probabilities as hi + lo bf16 pairs); longer ones the fast form (one bf16
+// query). Over a few thousand tokens the bf16 roundings of the query and of P
+// average out to well inside the error bar of the fp32 reference; below that they do
+// not, and a short sequence costs little either way.
+constexpr int kPreciseBelow = 4096;
+constexpr int kMaxSplitsPerSeq = 1024;  // bound on a sequence's token ranges
+constexpr int kMinRaggedChunk = 256;    // tokens per range at least, ragged batches
+
 struct Plan {
-  int nw;        // 32-row blocks per attention workgroup (rows = 32 * nw)
-  bool roles;    // role-split 64-row form (rows not a multiple of 128)
-  int hgroups;   // workgroups per (sequence, split)
-  int n_splits;  // token ranges per sequence
-  int chunk;     // tokens per range, a multiple of kTile
-  int comb_rows;    // combine: query rows per workgroup (<= 32)
-  int comb_splits;  // combine: partial half rows staged per row and batch
-  int comb_slots;   // combine: staged half rows per batch (256, or 128 with two workgroups per CU)
-  bool ragged;      // host lengths given and not all equal
+  int fast_form;     // kForm128 (rows a multiple of 128) or kFormRoles
+  int fast_groups;   // head groups (workgroups) per pair in the fast form
+  int prec_groups;   // ... in the precise form (64-row workgroups)
+  int chunk;         // tokens per range, a multiple of kTile
+  int64_t cap;       // pairs the workspace holds: a bound on Σ_b ceil(kv_b / chunk)
+  int64_t fast_pairs, prec_pairs;  // bounds on the pairs of each list (0: not launched)
+  int comb_rows;     // combine: query rows per workgroup (<= 32)
 };
 
+int64_t ceil_div(int64_t x, int64_t y) { return (x + y - 1) / y; }
+
 Plan plan_bf16(const Resolved& r, const mla_decode_args* a) {
-  Plan p;
+  Plan p{};
   const int rows = r.h * a->n_q;
-  // 128-row workgroups when the rows come in 128s; else role-split 64-row workgroups
-  // (two score waves, two value waves)
-  p.roles = rows % 128 != 0;
-  p.nw = p.roles ? 2 : 4;
-  p.hgroups = rows / (32 * p.nw);
-  // one workgroup per CU either way: four tile buffers take most of the LDS
-  const int64_t target = 256;
-  const int L = a->max_kv_len;
-  const int64_t units = static_cast<int64_t>(a->batch) * p.hgroups;
-  // one workgroup per slot when every sequence is as long as the longest
-  int64_t split_target = std::max<int64_t>(1, (target + units - 1) / units);
-  if (a->num_splits > 0) {
-    split_target = a->num_splits;
-  } else if (a->kv_lens_host) {
-    int64_t total = 0;
-    for (int b = 0; b < a->batch; ++b) total += std::min(a->kv_lens_host[b], L);
-    if (total * 5 < static_cast<int64_t>(a->batch) * L * 4) {
-      // ragged batch: ranges sized so the batch yields about three workgroups per slot
-      // (measured on the ragged two-query workload: 1, 2, 3, 4 per slot give an
-      // attention kernel of 370, 332, 323, 335 us; more ranges balance the lengths
-      // better until the combine's extra partial rows outweigh it)
-      const int64_t per_wg = std::max<int64_t>(kTile, (total * p.hgroups + 3 * target - 1) / (3 * target));
-      split_target = std::max<int64_t>(1, (L + per_wg - 1) / per_wg);
+  p.fast_form = rows % 128 == 0 ? kForm128 : kFormRoles;
+  p.fast_groups = rows / (p.fast_form == kForm128 ? 128 : 64);
+  p.prec_groups = rows / 64;
+  const int64_t L = a->max_kv_len;
+  const int64_t target = 256;  // workgroups per wave of the chip: one per CU
+  auto groups_of = [&](int64_t kv) { return kv < kPreciseBelow ? p.prec_groups : p.fast_groups; };
+  bool ragged = false;
+  int64_t total = 0, total_units = 0;  // tokens, and tokens x head groups
+  if (a->kv_lens_host) {
+    for (int b = 0; b < a->batch; ++b) {
+      const int64_t kv = std::min<int64_t>(a->kv_lens_host[b], L);
+      total += kv;
+      total_units += kv * groups_of(kv);
     }
+    ragged = total * 5 < static_cast<int64_t>(a->batch) * L * 4;
   }
-  split_target = std::min<int64_t>(split_target, (L + kTile - 1) / kTile);
-  split_target = std::max<int64_t>(split_target, 1);
-  int64_t chunk = (L + split_target - 1) / split_target;
-  chunk = (chunk + kTile - 1) / kTile * kTile;
-  p.chunk = static_cast<int>(chunk);
-  p.n_splits = static_cast<int>((L + chunk - 1) / chunk);
-  // combine grid: (h, 2 latent halves, M / rows); halve the rows until the grid fills
-  // the CUs; splits staged per batch fill the 256 half-row slots
-  // with 16 or more query rows, workgroups of up to 16 rows that stage 128 half rows,
-  // two per CU (one stages while the other computes: measured faster at every such
-  // shape); else up to 32 rows and 256 half rows, so few rows take many splits at once
+  int64_t chunk;
+  if (a->num_splits > 0) {
+    chunk = ceil_div(L, a->num_splits);
+  } else if (ragged) {
+    // ranges sized so the batch yields about three workgroups per slot (measured on
+    // the ragged two-query workload: 1, 2, 3, 4 per slot give an attention kernel of
+    // 370, 332, 323, 335 us; more ranges balance the lengths better until the
+    // combine's extra partial rows outweigh it)
+    // (at least kMinRaggedChunk tokens, so the fp32 partials of a range stay well
+    // below the bytes of cache it reads)
+    chunk = std::max<int64_t>(kMinRaggedChunk, ceil_div(total_units, 3 * target));
+  } else {
+    // one workgroup per slot when every sequence is as long as the longest
+    const int64_t units = static_cast<int64_t>(a->batch) * groups_of(L);
+    chunk = ceil_div(L, std::min(ceil_div(target, units), ceil_div(L, kTile)));
+  }
+  chunk = std::max(chunk, ceil_div(L, kMaxSplitsPerSeq));
+  chunk = ceil_div(chunk, kTile) * kTile;
+  p.chunk = static_cast<int>(std::min<int64_t>(chunk, ceil_div(L, kTile) * kTile));
+  if (a->kv_lens_host) {
+    for (int b = 0; b < a->batch; ++b) {
+      const int64_t kv = std::min<int64_t>(a->kv_lens_host[b], L);
+      const int64_t ns = kv >= a->n_q ? ceil_div(kv, p.chunk) : 0;
+      p.cap += ns;
+      (kv < kPreciseBelow ? p.prec_pairs : p.fast_pairs) += ns;
+    }
+  } else {
+    // any length up to max_kv_len: both lists may fill
+    p.cap = static_cast<int64_t>(a->batch) * ceil_div(L, p.chunk);
+    p.fast_pairs = L >= kPreciseBelow ? p.cap : 0;
+    p.prec_pairs = p.cap;
+  }
+  // combine grid: (h, 2 latent halves, M / rows): halve the rows until the grid has
+  // two workgroups per CU
   const int M = a->batch * a->n_q;
-  p.comb_slots = M >= 16 ? 128 : 256;
-  p.comb_rows = std::min(p.comb_slots == 128 ? 16 : 32, M);
-  while (p.comb_rows > 1 && 2LL * r.h * ((M + p.comb_rows - 1) / p.comb_rows) < 256) p.comb_rows = (p.comb_rows + 1) / 2;
-  p.comb_splits = std::min(p.n_splits, p.comb_slots / p.comb_rows);
-  // ragged lengths: the combine reads the lengths before staging partial rows, so the
-  // rows of short sequences load only the splits that hold their tokens
-  p.ragged = false;
-  if (a->kv_lens_host)
-    for (int b = 1; b < a->batch; ++b) p.ragged |= a->kv_lens_host[b] != a->kv_lens_host[0];
+  p.comb_rows = std::min(32, M);
+  while (p.comb_rows > 1 && 2LL * r.h * ceil_div(M, p.comb_rows) < 2 * target) p.comb_rows = (p.comb_rows + 1) / 2;
   return p;
 }
 
 struct Workspace {
-  size_t q_cat, o_part, ml_part, gate, scores, o_lat, total;
+  size_t counts, seq_off, fast_list, prec_list, q_cat, q_lo, o_part, ml_part, gate, scores, o_lat, total;
 };
 
 Workspace layout_ws(const Resolved& r, const mla_decode_args* a, const Plan* p) {
@@ -125,11 +142,24 @@ Workspace layout_ws(const Resolved& r, const mla_decode_args* a, const Plan* p) 
   size_t off = 0;
   if (r.dtype == MLA_BF16) {
     const size_t row = 512 + r.d_r;
+    const size_t cap = static_cast<size_t>(std::max<int64_t>(p->cap, 1));
+    w.counts = off;
+    off = align_up(off + 2 * sizeof(int32_t));
+    w.seq_off = off;
+    off = align_up(off + (static_cast<size_t>(a->batch) + 1) * sizeof(int32_t));
+    w.fast_list = off;  // both lists always exist: the device plan may fill either
+    off = align_up(off + cap * sizeof(WorkItem));
+    w.prec_list = off;
+    off = align_up(off + cap * sizeof(WorkItem));
     w.q_cat = off;
     off = align_up(off + M * r.h * row * 2);
-    const size_t prow = static_cast<size_t>(a->batch) * p->n_splits * a->n_q * r.h;
+    if (p->prec_pairs > 0) {
+      w.q_lo = off;
+      off = align_up(off + M * r.h * row * 2);
+    }
+    const size_t prow = cap * a->n_q * r.h;
     w.o_part = off;
-    off = align_up(off + prow * 512 * 2);
+    off = align_up(off + prow * 512 * 4);
     w.ml_part = off;
     off = align_up(off + prow * 2 * 4);
     if (a->gate_x) {
@@ -161,11 +191,11 @@ mla_status check_decode(const Resolved& r, const mla_decode_args* a) {
       if (a->kv_lens_host[b] < a->n_q || a->kv_lens_host[b] > a->max_kv_len) return MLA_E_SHAPE;
   }
   if (r.dtype == MLA_BF16) {
-    const int rows = r.h * a->n_q;
-    if (rows % 64 != 0) return MLA_E_UNSUPPORTED;
-    const int R = rows % 128 == 0 ? 128 : 64;
-    if (R % a->n_q != 0 || r.h % (R / a->n_q) != 0) return MLA_E_UNSUPPORTED;
-    if (a->gate_x && (a->d_model % (kGateSplit * 16) != 0 || (r.h * 128) % 128 != 0)) return MLA_E_UNSUPPORTED;
+    // 32-head query blocks, 64 or 128 rows per attention workgroup
+    if (r.h % 32 != 0 || (static_cast<int64_t>(r.h) * a->n_q) % 64 != 0) return MLA_E_UNSUPPORTED;
+    if (a->gate_x && a->d_model % (kGateSplit * 16) != 0) return MLA_E_UNSUPPORTED;
+    // every grid dimension and element offset the kernels form stays in range
+    if (static_cast<int64_t>(a->batch) * a->n_q > (int64_t(1) << 24) || r.h > 4096) return MLA_E_UNSUPPORTED;
   }
   return MLA_OK;
 }
@@ -222,21 +252,45 @@ mla_status decode_impl(const mla_dims* dims, const CacheRef& cache, const mla_de
 
   const uint16_t* w_uk_pk = static_cast<const uint16_t*>(a->packed_w);
   const uint16_t* w_uv_pk = w_uk_pk + static_cast<size_t>(r.h) * 8192 * 8;
+  // grids: the pairs a list may hold x head groups, padded to a multiple of 8 (one
+  // run of units per XCD; the extra workgroups find no pair and return)
+  auto grid_units = [](int64_t pairs, int groups) -> int64_t {
+    const int64_t u = pairs * groups;
+    return u >= 8 ? (u + 7) / 8 * 8 : u;
+  };
+  const int64_t fast_units = grid_units(p.fast_pairs, p.fast_groups);
+  const int64_t prec_units = grid_units(p.prec_pairs, p.prec_groups);
+  if (fast_units > INT32_MAX || prec_units > INT32_MAX || p.cap > INT32_MAX) return MLA_E_UNSUPPORTED;
+
+  int32_t* counts = reinterpret_cast<int32_t*>(wsb + ws.counts);
+  WorkItem* fast_list = reinterpret_cast<WorkItem*>(wsb + ws.fast_list);
+  WorkItem* prec_list = reinterpret_cast<WorkItem*>(wsb + ws.prec_list);
   QPrepArgs q{};
   q.q_nope = static_cast<const uint16_t*>(a->q_nope);
   q.q_rope = static_cast<const uint16_t*>(a->q_rope);
   q.w_uk_pk = w_uk_pk;
   q.kv_lens = a->kv_lens;
   q.q_cat = reinterpret_cast<uint16_t*>(wsb + ws.q_cat);
+  q.q_lo = p.prec_pairs > 0 ? reinterpret_cast<uint16_t*>(wsb + ws.q_lo) : nullptr;
   q.M = M;
   q.n_q = a->n_q;
   q.h = r.h;
   q.d_r = r.d_r;
   q.max_kv_len = a->max_kv_len;
-  q.rows_per_wg = 32 * p.nw;
   q.out = a->out;  // zeroed here: the combine adds its two latent halves into it
   q.qscale = qscale;
   for (int k = 0; k < r.d_r / 2 && k < 32; ++k) q.inv_freq[k] = pow(r.rope_base, -2.0 * k / r.d_r);
+  q.plan.kv_lens = a->kv_lens;
+  q.plan.batch = a->batch;
+  q.plan.n_q = a->n_q;
+  q.plan.max_kv_len = a->max_kv_len;
+  q.plan.chunk = p.chunk;
+  q.plan.precise_below = kPreciseBelow;
+  q.plan.cap = static_cast<int32_t>(p.cap);
+  q.plan.counts = counts;
+  q.plan.seq_off = reinterpret_cast<int32_t*>(wsb + ws.seq_off);
+  q.plan.fast = fast_list;
+  q.plan.precise = prec_list;
   if (launch_qprep_bf16(q, stream) != hipSuccess) return MLA_E_HIP;
 
   if (a->gate_x) {
@@ -251,26 +305,40 @@ mla_status decode_impl(const mla_dims* dims, const CacheRef& cache, const mla_de
     if (launch_splitk_gemm_bf16(g, stream) != hipSuccess) return MLA_E_HIP;
   }
 
+  // the attention launches: the fast form over the long sequences' pairs, then the
+  // precise form over the short ones'; the timing events bracket both
   DecodeArgs d{};
   d.cache = cache;
-  d.kv_lens = a->kv_lens;
   d.q_cat = q.q_cat;
-  d.o_part = reinterpret_cast<uint16_t*>(wsb + ws.o_part);
+  d.q_lo = q.q_lo;
+  d.o_part = reinterpret_cast<float*>(wsb + ws.o_part);
   d.ml_part = reinterpret_cast<float*>(wsb + ws.ml_part);
-  d.batch = a->batch;
   d.n_q = a->n_q;
   d.h = r.h;
   d.d_r = r.d_r;
-  d.n_splits = p.n_splits;
   d.chunk = p.chunk;
-  d.max_kv_len = a->max_kv_len;
-  d.role_split = p.roles ? 1 : 0;
-  if (launch_decode_bf16(d, stream, a->ev_attn_begin, a->ev_attn_end) != hipSuccess) return MLA_E_HIP;
+  const bool two = fast_units > 0 && prec_units > 0;
+  if (fast_units > 0) {
+    d.list = fast_list;
+    d.count = counts;
+    d.form = p.fast_form;
+    d.units = static_cast<int32_t>(fast_units);
+    if (launch_decode_bf16(d, stream, a->ev_attn_begin, two ? nullptr : a->ev_attn_end) != hipSuccess)
+      return MLA_E_HIP;
+  }
+  if (prec_units > 0) {
+    d.list = prec_list;
+    d.count = counts + 1;
+    d.form = kFormPrecise;
+    d.units = static_cast<int32_t>(prec_units);
+    if (launch_decode_bf16(d, stream, two ? nullptr : a->ev_attn_begin, a->ev_attn_end) != hipSuccess)
+      return MLA_E_HIP;
+  }
 
   CombineArgs c{};
   c.o_part = d.o_part;
   c.ml_part = d.ml_part;
-  c.kv_lens = a->kv_lens;
+  c.seq_off = q.plan.seq_off;
   c.w_uv_pk = w_uv_pk;
   c.gate = a->gate_x ? reinterpret_cast<const float*>(wsb + ws.gate) : nullptr;
   c.out = a->out;
@@ -278,13 +346,7 @@ mla_status decode_impl(const mla_dims* dims, const CacheRef& cache, const mla_de
   c.batch = a->batch;
   c.n_q = a->n_q;
   c.h = r.h;
-  c.n_splits = p.n_splits;
-  c.chunk = p.chunk;
-  c.max_kv_len = a->max_kv_len;
   c.rows_per_wg = p.comb_rows;
-  c.splits_per_batch = p.comb_splits;
-  c.slots = p.comb_slots;
-  c.lengths_first = p.ragged ? 1 : 0;
   return launch_combine_bf16(c, stream) == hipSuccess ? MLA_OK : MLA_E_HIP;
 }
 

@@ -49,8 +49,15 @@
 // row's reference (at most 8 times). The decision is workgroup-uniform, so every
 // wave takes the same barriers.
 //
-// Output per (b, split): the normalised partial O/l as bf16 rows of 512 (written
-// coalesced through LDS) and (m, l) in fp32; the combine kernel merges splits.
+// Output per (sequence, token range): the partial O (relative to each row's
+// reference m, not yet divided by l) as fp32 rows of 512, stored straight from the
+// accumulators, and (m, l) in fp32; the combine kernel merges the ranges.
+//
+// Work: a launch takes the (sequence, range) pairs of one list the query
+// preparation built on the device; workgroup u takes pair u / groups and head
+// group u % groups (XCD-aware: each XCD gets a contiguous run of units, so one
+// sequence's ranges and head groups share an L2). A workgroup's R rows are R / 32
+// consecutive 32-row query blocks of its sequence (block = one query x 32 heads).
 #include "common.hpp"
 #include "launch.hpp"
 #include <hip/hip_ext.h>
@@ -81,7 +88,6 @@ struct Cfg {
   static constexpr int CBW = 16 / NW;                      // value column blocks per wave
   static constexpr int RB = NW;                            // row blocks of 32 query rows
   static_assert((kTileT * CH) % (64 * NW) == 0, "tile loads per wave");
-  static_assert(32 * CBW * R * 2 <= TILE_BYTES, "epilogue staging fits a tile buffer");
 };
 
 template <int V>
@@ -104,6 +110,15 @@ __device__ __forceinline__ void mfma_v_last(f32x16& c, const u32x4& a, const u32
       : "+v"(c) : "v"(a), "v"(b));
 }
 
+// The same with the B operand in AGPRs (the precise form's low query halves).
+__device__ __forceinline__ void mfma_va(f32x16& c, const u32x4& a, const u32x4& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_va_last(f32x16& c, const u32x4& a, const u32x4& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 4"
+      : "+v"(c) : "v"(a), "a"(b));
+}
+
 }  // namespace
 
 template <int NW, int DR>
@@ -117,37 +132,34 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) char s_tile2[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char s_tile3[C::TILE_BYTES];
   // P fragments [parity][row block][k-step][lane]: P of tile i goes into buffer i % 2,
-  // so publishing it never waits for readers of tile i - 1's P. After the last step's
-  // barrier, the buffer the last tile did not use holds 1 / l per row.
+  // so publishing it never waits for readers of tile i - 1's P.
   constexpr int PBUF = RB * 2 * 1024;
   __shared__ __attribute__((aligned(16))) char s_p[2 * PBUF];
   static_assert(4 * C::TILE_BYTES + 2 * PBUF <= 160 * 1024, "LDS");
-  static_assert(16 + 4 * C::R <= PBUF, "1 / l fits a P buffer");
 
   const int tid = threadIdx.x, l = tid % 64;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64);  // wave index, uniform
   const int hgroups = (a.h * a.n_q) / C::R;
-  const int units = a.batch * a.n_splits * hgroups;
+  const int HB = a.h / 32;  // 32-head blocks per query
 
   // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous
   // range of units so one sequence's splits (and head groups) share an L2.
   int u = blockIdx.x;
-  if ((units & 7) == 0) u = (blockIdx.x & 7) * (units >> 3) + (blockIdx.x >> 3);
-  const int hg = u % hgroups;
-  const int s = (u / hgroups) % a.n_splits;
-  const int b = u / (hgroups * a.n_splits);
-
-  const int kv = min(a.kv_lens[b], a.max_kv_len);
-  const int t_begin = s * a.chunk;
+  if ((a.units & 7) == 0) u = (blockIdx.x & 7) * (a.units >> 3) + (blockIdx.x >> 3);
+  const int pair = u / hgroups, hg = u - pair * hgroups;
+  if (pair >= *a.count) return;  // uniform: past the pairs of this launch
+  const WorkItem item = a.list[pair];
+  const int b = item.b, kv = item.kv;
+  const int t_begin = item.s * a.chunk;
   const int t_end = min(t_begin + a.chunk, kv);
-  if (t_begin >= t_end || kv < a.n_q) return;  // empty split: the combine skips it
+  if (t_begin >= t_end || kv < a.n_q) return;  // not listed by the plan
   const int n_tiles = (t_end - t_begin + kTileT - 1) / kTileT;
 
-  const int HG = C::R / a.n_q;  // heads per workgroup
-  // this lane's score row r = 32w + l%32 (lanes l and l^32 hold the same row)
-  const int r_own = 32 * w + (l & 31);
-  const int j_own = r_own / HG;
-  const int head_own = hg * HG + r_own % HG;
+  // wave w's score rows: query block qb_own = RB hg + w of the sequence, i.e. query
+  // j_own and heads 32 (qb_own % HB) + l%32 (lanes l and l^32 hold the same row)
+  const int qb_own = RB * hg + w;
+  const int j_own = qb_own / HB;
+  const int head_own = 32 * (qb_own - j_own * HB) + (l & 31);
   const int vis_own = kv - a.n_q + j_own;  // last visible position of this row
 
   // ---- tile loads: wave load n' = n*NW + w fills LDS [n'*1024, +1024) = column
@@ -438,7 +450,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   {
     // Q_cat is stored in this kernel's fragment order: one 1 KiB wave load per k-step
     const u32x4* qp = reinterpret_cast<const u32x4*>(a.q_cat) +
-                      ((static_cast<int64_t>(b) * hgroups + hg) * NW + w) * C::KS * 64 + l;
+                      (static_cast<int64_t>(b) * a.n_q * HB + qb_own) * C::KS * 64 + l;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) qf[ks] = qp[ks * 64];
   }
@@ -486,60 +498,40 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     m_ref = m_seen;
   }
 
-  // ---- epilogue: normalised partial O/l as bf16 rows. 1/l of each row comes from
-  //      its score wave; each wave stages its 32*CBW columns of all R rows in its
-  //      own tile buffer ([R rows][4*CBW chunks], chunk ^ (row & 15)) and writes
-  //      them out as contiguous row segments.
-  // 1 / l per row, in the P buffer the last tile did not use (free since the barrier
-  // after the last step; the staging below starts after the next barrier)
-  float* s_inv = reinterpret_cast<float*>(s_p + (n_tiles & 1) * PBUF + 16);
-  if (l < 32) s_inv[r_own] = l_run > 0.f ? 1.f / l_run : 0.f;
-  lds_barrier();  // every wave is past the last tile; s_inv complete
-  constexpr int CPR = 4 * CBW;  // 16-byte chunks per staged row
-  constexpr int RSB = 16 * CPR;  // staged row bytes
-  char* stg = w == 0 ? s_tile0 : w == 1 ? s_tile1 : w == 2 ? s_tile2 : s_tile3;
+  // ---- epilogue: the partial O of this wave's columns for every row block, fp32,
+  //      straight from the accumulators: lane l holds row l%32 of a block and 4
+  //      adjacent columns per 4 values, so a store writes 32 bytes of each of 32 rows
+  //      and four of them complete the rows' 128-byte column block. (m, l) of each
+  //      row comes from its score lane.
+  const int64_t prow0 = static_cast<int64_t>(item.p) * a.n_q;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const int row = 32 * rb + (l & 31);
-    const float inv = s_inv[row];
+    const int qb = RB * hg + rb, j = qb / HB;
+    const int head = 32 * (qb - j * HB) + (l & 31);
+    float* dst = a.o_part + ((prow0 + j) * a.h + head) * 512 + 32 * CBW * w + 4 * (l >> 5);
 #pragma unroll
     for (int cbl = 0; cbl < CBW; ++cbl)
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
         const f32x16& o = acc[cbl * RB + rb];
-        const int chunk = (4 * cbl + v4) ^ (row & 15);
-        const u32x2 v2 = {pack_bf16x2(o[4 * v4] * inv, o[4 * v4 + 1] * inv),
-                          pack_bf16x2(o[4 * v4 + 2] * inv, o[4 * v4 + 3] * inv)};
-        *(lds_u32x2*)(lds_ptr(stg) + row * RSB + chunk * 16 + (l >> 5) * 8) = v2;
+        *reinterpret_cast<f32x4*>(dst + 32 * cbl + 8 * v4) = f32x4{o[4 * v4], o[4 * v4 + 1], o[4 * v4 + 2], o[4 * v4 + 3]};
       }
   }
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging writes are done
-  __builtin_amdgcn_wave_barrier();
-  const int64_t part_row0 = (static_cast<int64_t>(b) * a.n_splits + s) * a.n_q;
-  constexpr int RPI = 64 / CPR;  // rows per wave instruction
-#pragma unroll 4
-  for (int q = 0; q < C::R / RPI; ++q) {
-    const int row = RPI * q + l / CPR, ch = l % CPR;
-    const int j = row / HG, head = hg * HG + row % HG;
-    const u32x4 v = *(lds_u32x4*)(lds_ptr(stg) + row * RSB + ((ch ^ (row & 15)) << 4));
-    *reinterpret_cast<u32x4*>(a.o_part + ((part_row0 + j) * a.h + head) * 512 + 32 * CBW * w + ch * 8) = v;
-  }
   if (l < 32) {
-    float* ml = a.ml_part + ((part_row0 + j_own) * a.h + head_own) * 2;
+    float* ml = a.ml_part + ((prow0 + j_own) * a.h + head_own) * 2;
     ml[0] = m_ref;
     ml[1] = l_run;
   }
 }
 
 // Role-split form for 64 query rows per workgroup (a (sequence, token range, head
-// group) unit of 64 rows). Waves 0-1 own the scores and the softmax of rows
-// 32w .. 32w + 31 (their Q_cat fragments in VGPRs, the same fragment order as the
-// 64-row workgroups above). Waves 2-3 own the value contraction for latent columns
-// 256 v .. 256 v + 255 (v = w - 2) of all 64 rows (Oᵀ: 16 blocks of 32x32 fp32 in
-// AGPRs) and issue every tile load. Both pairs run about 1.1k MFMA cycles per tile,
-// so the matrix cores of all four SIMDs stay busy, while a unit holds half the rows
-// of the 128-row form: a sequence needs half as many token ranges for the same
-// number of workgroups, which halves the split partials the combine reads back.
+// group) unit of two 32-row query blocks). Waves 0-1 own the scores and the softmax
+// of block w (its Q_cat fragments in VGPRs). Waves 2-3 own the value contraction for
+// latent columns 256 v .. 256 v + 255 (v = w - 2) of all 64 rows (Oᵀ: 16 blocks of
+// 32x32 fp32 in AGPRs) and issue every tile load. Both pairs run about 1.1k MFMA
+// cycles per tile, so the matrix cores of all four SIMDs stay busy, while a unit
+// holds half the rows of the 128-row form: a sequence needs half as many token
+// ranges for the same number of workgroups, which halves the split partials.
 //
 // Step i (one barrier): the value waves wait for their share of tile i, everyone
 // passes the barrier; the value waves issue tile i + 2 into the buffer of tile
@@ -547,7 +539,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 // waves run tile i's score chain and softmax and publish P into buffer i % 2. P
 // buffer i % 2 held tile i - 2's P, which the value waves finished reading in step
 // i - 1. Restarts, masking and the output are as in the 128-row form.
-template <int DR>
+//
+// PRECISE: the query and the probabilities each enter the matrix cores as a pair of
+// bf16 values, hi = bf16(x) and lo = bf16(x - hi), so both contractions see about 16
+// significant bits of them (the cache is bf16 already). The score waves keep the
+// low query halves in their AGPRs, which the role split leaves free on those waves,
+// and run two MFMAs per fragment of the tile (it is read once); the value waves
+// read a low P buffer beside the high one and run two MFMAs per cache fragment.
+// This form serves the sequences too short for bf16 rounding of the query and of
+// P to average out (the host plan sends them here).
+template <int DR, bool PRECISE>
 __global__ __launch_bounds__(256) void decode_roles_kernel(DecodeArgs a) {
   constexpr int ROW = 512 + DR, ROWB = ROW * 2, CH = ROW / 8, KS = ROW / 16;
   constexpr int R = 64;                           // query rows per workgroup
@@ -556,38 +557,37 @@ __global__ __launch_bounds__(256) void decode_roles_kernel(DecodeArgs a) {
   constexpr int CBW = 8;                          // value column blocks per value wave
   constexpr int RB = 2;                           // row blocks of 32 query rows
   static_assert((kTileT * CH) % 128 == 0, "tile loads per value wave");
-  static_assert(R * 256 * 2 <= TILE_BYTES, "a value wave's staged rows fit a tile buffer");
   __shared__ __attribute__((aligned(1024))) char s_tile0[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char s_tile1[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char s_tile2[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char s_tile3[TILE_BYTES];
   constexpr int PBUF = RB * 2 * 1024;  // P fragments [row block][k-step][lane]
-  __shared__ __attribute__((aligned(16))) char s_p[2 * PBUF];
-  static_assert(4 * TILE_BYTES + 2 * PBUF <= 160 * 1024, "LDS");
-  static_assert(16 + 4 * R <= PBUF, "1 / l fits a P buffer");
+  // [parity] high P, then (PRECISE) [parity] low P
+  __shared__ __attribute__((aligned(16))) char s_p[(PRECISE ? 4 : 2) * PBUF];
+  static_assert(4 * TILE_BYTES + (PRECISE ? 4 : 2) * PBUF <= 160 * 1024, "LDS");
 
   const int tid = threadIdx.x, l = tid % 64;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64);  // wave index, uniform
   const bool scorer = w < 2;
   const int vw = w - 2;  // value wave index (value waves only)
   const int hgroups = (a.h * a.n_q) / R;
-  const int units = a.batch * a.n_splits * hgroups;
+  const int HB = a.h / 32;
   int u = blockIdx.x;
-  if ((units & 7) == 0) u = (blockIdx.x & 7) * (units >> 3) + (blockIdx.x >> 3);
-  const int hg = u % hgroups;
-  const int s = (u / hgroups) % a.n_splits;
-  const int b = u / (hgroups * a.n_splits);
-
-  const int kv = min(a.kv_lens[b], a.max_kv_len);
-  const int t_begin = s * a.chunk;
+  if ((a.units & 7) == 0) u = (blockIdx.x & 7) * (a.units >> 3) + (blockIdx.x >> 3);
+  const int pair = u / hgroups, hg = u - pair * hgroups;
+  if (pair >= *a.count) return;  // uniform: past the pairs of this launch
+  const WorkItem item = a.list[pair];
+  const int b = item.b, kv = item.kv;
+  const int t_begin = item.s * a.chunk;
   const int t_end = min(t_begin + a.chunk, kv);
-  if (t_begin >= t_end || kv < a.n_q) return;  // empty split: the combine skips it
+  if (t_begin >= t_end || kv < a.n_q) return;  // not listed by the plan
   const int n_tiles = (t_end - t_begin + kTileT - 1) / kTileT;
 
-  const int HG = R / a.n_q;  // heads per workgroup
-  const int r_own = 32 * (w & 1) + (l & 31);  // score waves: this lane's row
-  const int j_own = r_own / HG;
-  const int head_own = hg * HG + r_own % HG;
+  // score wave w: query block qb_own = 2 hg + w of the sequence (query j_own, heads
+  // 32 (qb_own % HB) + l%32)
+  const int qb_own = RB * hg + (w & 1);
+  const int j_own = qb_own / HB;
+  const int head_own = 32 * (qb_own - j_own * HB) + (l & 31);
   const int vis_own = kv - a.n_q + j_own;
 
   // ---- tile loads (value waves): wave load n' = 2n + v fills LDS [n'*1024, +1024) =
@@ -638,15 +638,16 @@ __global__ __launch_bounds__(256) void decode_roles_kernel(DecodeArgs a) {
     else if constexpr (K == 2) return s_tile2;
     else return s_tile3;
   };
-  const int64_t part_row0 = (static_cast<int64_t>(b) * a.n_splits + s) * a.n_q;
+  const int64_t prow0 = static_cast<int64_t>(item.p) * a.n_q;
 
   // The two roles run as separate copies of the loop (the branch is taken once, so
   // the score waves' Q fragments and the value waves' accumulators never share a
   // live range); both copies pass the same barriers in the same order.
   auto run = [&](auto role) __attribute__((always_inline)) {
     constexpr bool SC = decltype(role)::value != 0;
-    u32x4 qf[SC ? KS : 1];           // score waves: this row's Q_cat fragments
-    f32x16 acc[SC ? 1 : CBW * RB];   // value waves: Oᵀ, acc[cbl * RB + rb]
+    u32x4 qf[SC ? KS : 1];                  // score waves: this row's Q_cat fragments
+    u32x4 ql[SC && PRECISE ? KS : 1];       // score waves, PRECISE: low halves (AGPRs)
+    f32x16 acc[SC ? 1 : CBW * RB];          // value waves: Oᵀ, acc[cbl * RB + rb]
     float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
     uint64_t ovr = 0;
     int pg_next = 0;
@@ -686,8 +687,14 @@ __global__ __launch_bounds__(256) void decode_roles_kernel(DecodeArgs a) {
       for (int ks = 0; ks < SDEPTH; ++ks) fa[ks] = frag(ks);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        if (ks + 1 < KS) mfma_v(sc, fa[ks % SDEPTH], qf[ks]);
-        else mfma_v_last(sc, fa[ks % SDEPTH], qf[ks]);
+        if constexpr (PRECISE) {
+          mfma_v(sc, fa[ks % SDEPTH], qf[ks]);
+          if (ks + 1 < KS) mfma_va(sc, fa[ks % SDEPTH], ql[ks]);
+          else mfma_va_last(sc, fa[ks % SDEPTH], ql[ks]);
+        } else {
+          if (ks + 1 < KS) mfma_v(sc, fa[ks % SDEPTH], qf[ks]);
+          else mfma_v_last(sc, fa[ks % SDEPTH], qf[ks]);
+        }
         if (ks + SDEPTH < KS) fa[ks % SDEPTH] = frag(ks + SDEPTH);
       }
       return sc;
@@ -702,9 +709,9 @@ __global__ __launch_bounds__(256) void decode_roles_kernel(DecodeArgs a) {
       }
     };
     // softmax of a tile against the row's fixed reference: P as 8 packed bf16 pairs
-    // (values 2k, 2k + 1 of the score accumulator); `overrun` if a score passed it by
-    // more than the headroom
-    auto softmax = [&](const f32x16& sc, bool allow_restart, u32x4* p) __attribute__((always_inline)) -> bool {
+    // (values 2k, 2k + 1 of the score accumulator), and (PRECISE) the low halves in
+    // p_lo; `overrun` if a score passed the reference by more than the headroom
+    auto softmax = [&](const f32x16& sc, bool allow_restart, u32x4* p, u32x4* p_lo) __attribute__((always_inline)) -> bool {
       const float m0 = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
       const float m1 = fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7]));
       const float m2 = fmaxf(fmaxf(sc[8], sc[9]), fmaxf(sc[10], sc[11]));
@@ -718,7 +725,10 @@ __global__ __launch_bounds__(256) void decode_roles_kernel(DecodeArgs a) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const float p0 = fast_exp2(sc[2 * q] - mref), p1 = fast_exp2(sc[2 * q + 1] - mref);
-        p[q >> 2][q & 3] = pack_bf16x2(p0, p1);
+        const uint32_t hi = pack_bf16x2(p0, p1);
+        p[q >> 2][q & 3] = hi;
+        if constexpr (PRECISE)
+          p_lo[q >> 2][q & 3] = pack_bf16x2(p0 - __uint_as_float(hi << 16), p1 - __uint_as_float(hi & 0xFFFF0000u));
         ps[q & 3] += p0 + p1;
       }
       l_run += half_sum((ps[0] + ps[1]) + (ps[2] + ps[3]));
@@ -740,18 +750,24 @@ __global__ __launch_bounds__(256) void decode_roles_kernel(DecodeArgs a) {
       i16x8 frag[WIN];
 #pragma unroll
       for (int f = 0; f < WIN; ++f) frag[f] = load(f);
-      u32x4 pb[RB];
+      u32x4 pb[RB], pbl[PRECISE ? RB : 1];
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
         const int kk = f / CBW, cbl = f % CBW;
         if (cbl == 0) {
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) pb[rb] = *(lds_u32x4*)(lds_ptr(pbuf) + (rb * 2 + kk) * 1024 + l * 16);
+          for (int rb = 0; rb < RB; ++rb) {
+            pb[rb] = *(lds_u32x4*)(lds_ptr(pbuf) + (rb * 2 + kk) * 1024 + l * 16);
+            if constexpr (PRECISE) pbl[rb] = *(lds_u32x4*)(lds_ptr(pbuf) + 2 * PBUF + (rb * 2 + kk) * 1024 + l * 16);
+          }
         }
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           acc[cbl * RB + rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               __builtin_bit_cast(bf16x8, frag[f % WIN]), as_bf16x8(pb[rb]), acc[cbl * RB + rb], 0, 0, 0);
+          if constexpr (PRECISE)
+            acc[cbl * RB + rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, frag[f % WIN]), as_bf16x8(pbl[rb]), acc[cbl * RB + rb], 0, 0, 0);
           if (rb == RB - 1 && f + WIN < NF) frag[f % WIN] = load(f + WIN);
         }
       }
@@ -770,11 +786,16 @@ __global__ __launch_bounds__(256) void decode_roles_kernel(DecodeArgs a) {
       } else {
         f32x16 sc = scores(tile_ptr(kc));
         if (i >= first_masked) apply_mask(sc, i);  // uniform
-        u32x4 p[2];
-        const bool overrun = softmax(sc, allow_restart, p);
+        u32x4 p[2], p_lo[2];
+        const bool overrun = softmax(sc, allow_restart, p, p_lo);
         ovr |= __builtin_amdgcn_ballot_w64(overrun);
-        *(lds_u32x4*)(lds_ptr(s_p + (K & 1) * PBUF) + (w * 2 + 0) * 1024 + l * 16) = p[0];
-        *(lds_u32x4*)(lds_ptr(s_p + (K & 1) * PBUF) + (w * 2 + 1) * 1024 + l * 16) = p[1];
+        char* pd = s_p + (K & 1) * PBUF;
+        *(lds_u32x4*)(lds_ptr(pd) + (w * 2 + 0) * 1024 + l * 16) = p[0];
+        *(lds_u32x4*)(lds_ptr(pd) + (w * 2 + 1) * 1024 + l * 16) = p[1];
+        if constexpr (PRECISE) {
+          *(lds_u32x4*)(lds_ptr(pd) + 2 * PBUF + (w * 2 + 0) * 1024 + l * 16) = p_lo[0];
+          *(lds_u32x4*)(lds_ptr(pd) + 2 * PBUF + (w * 2 + 1) * 1024 + l * 16) = p_lo[1];
+        }
       }
     };
     auto prologue = [&]() __attribute__((always_inline)) {
@@ -787,10 +808,15 @@ __global__ __launch_bounds__(256) void decode_roles_kernel(DecodeArgs a) {
 
     prologue();
     if constexpr (SC) {
-      const u32x4* qp = reinterpret_cast<const u32x4*>(a.q_cat) +
-                        ((static_cast<int64_t>(b) * hgroups + hg) * 2 + w) * KS * 64 + l;
+      const int64_t qoff = (static_cast<int64_t>(b) * a.n_q * HB + qb_own) * KS * 64 + l;
+      const u32x4* qp = reinterpret_cast<const u32x4*>(a.q_cat) + qoff;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qf[ks] = qp[ks * 64];
+      if constexpr (PRECISE) {
+        const u32x4* qlp = reinterpret_cast<const u32x4*>(a.q_lo) + qoff;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) ql[ks] = qlp[ks * 64];
+      }
       wait_vm<0>();
     }
     for (int pass = 0;; ++pass) {
@@ -832,46 +858,27 @@ __global__ __launch_bounds__(256) void decode_roles_kernel(DecodeArgs a) {
       m_ref = m_seen;
     }
 
-    // ---- epilogue: 1 / l of each row from the score waves; each value wave stages
-    //      its 256 columns of the 64 rows in tile buffer v ([64 rows][32 chunks],
-    //      chunk ^ (row & 31)) and writes them out as contiguous 512-byte row segments
-    float* s_inv = reinterpret_cast<float*>(s_p + (n_tiles & 1) * PBUF + 16);
-    if constexpr (SC) {
-      if (l < 32) s_inv[r_own] = l_run > 0.f ? 1.f / l_run : 0.f;
-    }
-    lds_barrier();  // every wave is past the last tile; s_inv complete
+    // ---- epilogue: value waves store the partial O of their 256 columns for both
+    //      row blocks (fp32, straight from the accumulators, as in the 128-row
+    //      form); score waves store (m, l) of their rows
     if constexpr (!SC) {
-      constexpr int CPR = 4 * CBW;   // 16-byte chunks per staged row (32)
-      constexpr int RSB = 16 * CPR;  // staged row bytes (512)
-      char* stg = vw == 0 ? s_tile0 : s_tile1;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const int row = 32 * rb + (l & 31);
-        const float inv = s_inv[row];
+        const int qb = RB * hg + rb, j = qb / HB;
+        const int head = 32 * (qb - j * HB) + (l & 31);
+        float* dst = a.o_part + ((prow0 + j) * a.h + head) * 512 + 256 * vw + 4 * (l >> 5);
 #pragma unroll
         for (int cbl = 0; cbl < CBW; ++cbl)
 #pragma unroll
           for (int v4 = 0; v4 < 4; ++v4) {
             const f32x16& o = acc[cbl * RB + rb];
-            const int chunk = (4 * cbl + v4) ^ (row & 31);
-            const u32x2 v2 = {pack_bf16x2(o[4 * v4] * inv, o[4 * v4 + 1] * inv),
-                              pack_bf16x2(o[4 * v4 + 2] * inv, o[4 * v4 + 3] * inv)};
-            *(lds_u32x2*)(lds_ptr(stg) + row * RSB + chunk * 16 + (l >> 5) * 8) = v2;
+            *reinterpret_cast<f32x4*>(dst + 32 * cbl + 8 * v4) =
+                f32x4{o[4 * v4], o[4 * v4 + 1], o[4 * v4 + 2], o[4 * v4 + 3]};
           }
-      }
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging writes are done
-      __builtin_amdgcn_wave_barrier();
-      constexpr int RPI = 64 / CPR;  // rows per wave instruction (2)
-#pragma unroll 4
-      for (int q = 0; q < R / RPI; ++q) {
-        const int row = RPI * q + l / CPR, ch = l % CPR;
-        const int j = row / HG, head = hg * HG + row % HG;
-        const u32x4 v = *(lds_u32x4*)(lds_ptr(stg) + row * RSB + ((ch ^ (row & 31)) << 4));
-        *reinterpret_cast<u32x4*>(a.o_part + ((part_row0 + j) * a.h + head) * 512 + 256 * vw + ch * 8) = v;
       }
     } else {
       if (l < 32) {
-        float* ml = a.ml_part + ((part_row0 + j_own) * a.h + head_own) * 2;
+        float* ml = a.ml_part + ((prow0 + j_own) * a.h + head_own) * 2;
         ml[0] = m_ref;
         ml[1] = l_run;
       }
@@ -885,25 +892,27 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s, hipEvent_t ev0
   // hipExtLaunchKernelGGL stamps ev0/ev1 from the dispatch itself, so an event pair
   // brackets exactly this kernel's execution (null events: plain launch).
   const int rows = a.h * a.n_q;
-  if (a.role_split) {
-    if (rows % 64 != 0) return hipErrorInvalidValue;
-    const unsigned units = static_cast<unsigned>(a.batch * a.n_splits * (rows / 64));
-    if (a.d_r == 64)
-      hipExtLaunchKernelGGL(decode_roles_kernel<64>, dim3(units), dim3(256), 0, s, ev0, ev1, 0, a);
-    else if (a.d_r == 0)
-      hipExtLaunchKernelGGL(decode_roles_kernel<0>, dim3(units), dim3(256), 0, s, ev0, ev1, 0, a);
-    else
-      return hipErrorInvalidValue;
-    return hipGetLastError();
-  }
-  if (rows % 128 != 0) return hipErrorInvalidValue;
-  const unsigned units = static_cast<unsigned>(a.batch * a.n_splits * (rows / 128));
-  if (a.d_r == 64)
-    hipExtLaunchKernelGGL(decode_kernel<4, 64>, dim3(units), dim3(256), 0, s, ev0, ev1, 0, a);
-  else if (a.d_r == 0)
-    hipExtLaunchKernelGGL(decode_kernel<4, 0>, dim3(units), dim3(256), 0, s, ev0, ev1, 0, a);
-  else
+  const int R = a.form == kForm128 ? 128 : 64;
+  if (rows % R != 0 || a.h % 32 != 0 || a.units <= 0) return hipErrorInvalidValue;
+  if (a.form == kFormPrecise && a.q_lo == nullptr) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(a.units));
+#define MLA_LAUNCH(K) hipExtLaunchKernelGGL(K, grid, dim3(256), 0, s, ev0, ev1, 0, a)
+  if (a.form == kForm128) {
+    if (a.d_r == 64) MLA_LAUNCH((decode_kernel<4, 64>));
+    else if (a.d_r == 0) MLA_LAUNCH((decode_kernel<4, 0>));
+    else return hipErrorInvalidValue;
+  } else if (a.form == kFormRoles) {
+    if (a.d_r == 64) MLA_LAUNCH((decode_roles_kernel<64, false>));
+    else if (a.d_r == 0) MLA_LAUNCH((decode_roles_kernel<0, false>));
+    else return hipErrorInvalidValue;
+  } else if (a.form == kFormPrecise) {
+    if (a.d_r == 64) MLA_LAUNCH((decode_roles_kernel<64, true>));
+    else if (a.d_r == 0) MLA_LAUNCH((decode_roles_kernel<0, true>));
+    else return hipErrorInvalidValue;
+  } else {
     return hipErrorInvalidValue;
+  }
+#undef MLA_LAUNCH
   return hipGetLastError();
 }
 

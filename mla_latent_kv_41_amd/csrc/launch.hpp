@@ -23,45 +23,76 @@ hipError_t launch_append(int dtype, void* cache, const CacheRef& c, int batch, i
                          int d_r, const void* c_kv, const void* k_r, const int32_t* pos0,
                          double rope_base, hipStream_t s);
 
+// One (sequence, token range) pair of the split-K attention. The query
+// preparation writes the pairs of each class into a list on the device.
+struct WorkItem {
+  int32_t b;   // sequence
+  int32_t s;   // token range [s * chunk, min((s + 1) * chunk, kv))
+  int32_t p;   // partial index: the range's partial rows are (p * n_q + j) * h + head
+  int32_t kv;  // the sequence's length, clamped to max_kv_len
+};
+
+// Split plan built on the device (by the query preparation's first workgroup) from
+// kv_lens: sequence b holds ns_b = ceil(kv_b / chunk) ranges (none if kv_b < n_q);
+// their partials take indices seq_off[b] .. seq_off[b] + ns_b - 1, compactly. A
+// sequence with fewer than precise_below tokens goes to the precise list, else to
+// the fast list. Pairs past `cap` are dropped (only possible when the host lengths
+// the plan was sized from disagree with kv_lens).
+struct PlanArgs {
+  const int32_t* kv_lens;
+  int32_t batch, n_q, max_kv_len, chunk, precise_below, cap;
+  int32_t* counts;    // [0] pairs in the fast list, [1] in the precise list
+  int32_t* seq_off;   // [batch + 1]
+  WorkItem* fast;     // [cap]
+  WorkItem* precise;  // [cap]
+};
+
 struct QPrepArgs {
   const uint16_t* q_nope;   // [M][h][128]
   const uint16_t* q_rope;   // [M][h][64] or nullptr
   const uint16_t* w_uk_pk;  // packed W_UK
   const int32_t* kv_lens;
-  uint16_t* q_cat;          // fragment order of the attention kernel (see qprep_kernel)
+  uint16_t* q_cat;          // block order (see qprep_kernel): bf16 of the scaled query
+  uint16_t* q_lo;           // same order: bf16 of what q_cat's rounding left, or nullptr
   int32_t M, n_q, h, d_r, max_kv_len;
-  int32_t rows_per_wg;      // query rows per attention workgroup (32 per wave)
   float* out;               // [M][h*128] output, zeroed for the combine's atomic adds
   float qscale;             // scale * log2(e)
   double inv_freq[32];      // rope_base^(-2k/d_r), computed on the host in fp64
+  PlanArgs plan;
 };
 hipError_t launch_qprep_bf16(const QPrepArgs& a, hipStream_t s);
 
+// Attention kernel forms
+enum DecodeForm : int32_t {
+  kForm128 = 0,       // 128 query rows per workgroup, one bf16 query (fast)
+  kFormRoles = 1,     // role-split 64-row workgroups, one bf16 query (fast)
+  kFormPrecise = 2,   // role-split 64-row workgroups, query and probabilities as hi + lo bf16
+};
+
 struct DecodeArgs {
   CacheRef cache;
-  const int32_t* kv_lens;
-  const uint16_t* q_cat;  // fragment order (written by qprep_kernel)
-  uint16_t* o_part;       // [B][S][n_q][h][512] bf16, normalised O / l
-  float* ml_part;         // [B][S][n_q][h][2]
-  int32_t batch, n_q, h, d_r, n_splits, chunk, max_kv_len;
-  int32_t role_split;   // 1: role-split 64-row workgroups (h n_q % 128 == 64); 0: 128-row workgroups
+  const uint16_t* q_cat;   // block order (written by qprep_kernel)
+  const uint16_t* q_lo;    // kFormPrecise: the low halves, same order
+  const WorkItem* list;    // the pairs this launch takes
+  const int32_t* count;    // number of pairs in `list` (device)
+  float* o_part;           // [pairs][n_q][h][512] fp32, O relative to the row's reference m
+  float* ml_part;          // [pairs][n_q][h][2] (m, l), base-2 units
+  int32_t n_q, h, d_r, chunk;
+  int32_t form;            // DecodeForm
+  int32_t units;           // workgroups launched: pairs the list may hold x head groups
 };
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 
 struct CombineArgs {
-  const uint16_t* o_part;  // [B][S][n_q][h][512] bf16
-  const float* ml_part;    // [B][S][n_q][h][2] (m, l)
-  const int32_t* kv_lens;
+  const float* o_part;      // [pairs][n_q][h][512]
+  const float* ml_part;     // [pairs][n_q][h][2] (m, l)
+  const int32_t* seq_off;   // [batch + 1] first partial index of each sequence
   const uint16_t* w_uv_pk;  // packed W_UV
-  const float* gate;        // [M][h*128] pre-activation gate logits or nullptr
+  const float* gate;        // [16][M][h*128] pre-activation gate logit splits, or nullptr
   float* out;               // [M][h*128], zeroed beforehand: halves are added atomically
   float* lse;               // [M][h] or nullptr
-  int32_t batch, n_q, h, n_splits, chunk, max_kv_len;
-  int32_t rows_per_wg;       // query rows per workgroup, 1..32
-  int32_t splits_per_batch;  // half partial rows staged per row and batch (rows * splits <= slots)
-  int32_t slots;             // staged half rows per batch: 256, or 128 (two workgroups per CU)
-  int32_t lengths_first;     // 1: wait for the sequence lengths before staging, and skip the
-                             // partial rows of splits past each row's last one (ragged batches)
+  int32_t batch, n_q, h;
+  int32_t rows_per_wg;      // query rows per workgroup, 1..32
 };
 hipError_t launch_combine_bf16(const CombineArgs& a, hipStream_t s);
 

@@ -54,20 +54,64 @@ hipError_t launch_pack_bf16(const uint16_t* w_uk, const uint16_t* w_uv, uint16_t
   return hipGetLastError();
 }
 
-// Q_cat is written in the attention kernel's B-fragment order, so each of its
-// fragment loads is one contiguous 1 KiB wave read: element (row m, head i,
-// column c) sits in workgroup (b, hg) = (m / n_q, i / HG) with HG = R / n_q heads
-// per workgroup of R rows, at row r = (m % n_q) HG + i % HG, wave r / 32, k-step
-// c / 16, lane (r % 32) + 32 ((c / 8) % 2), element c % 8.
-__device__ __forceinline__ int64_t qfrag_off(const QPrepArgs& a, int m, int i, int c) {
-  const int KS = (512 + a.d_r) / 16;
-  const int HG = a.rows_per_wg / a.n_q;
-  const int hgroups = a.h / HG;
-  const int nw = a.rows_per_wg / 32;
-  const int b = m / a.n_q, j = m % a.n_q;
-  const int hg = i / HG, r = j * HG + i % HG;
-  const int lane = (r & 31) + 32 * ((c >> 3) & 1);
-  return ((((static_cast<int64_t>(b) * hgroups + hg) * nw + (r >> 5)) * KS + (c >> 4)) * 64 + lane) * 8 + (c & 7);
+// Q_cat is written in the attention kernels' B-fragment order, in blocks of 32
+// query rows: block (m, i / 32) holds query row m (= b * n_q + j) of heads
+// 32 (i / 32) .. + 31. Within a block, column c of head i sits at k-step c / 16,
+// lane (i % 32) + 32 ((c / 8) % 2), element c % 8, so each of an attention wave's
+// fragment loads is one contiguous 1 KiB read. An attention workgroup takes
+// consecutive blocks of one sequence; blocks of one query are consecutive.
+//
+// Precise mode (q_lo != nullptr): q_lo holds bf16(x - bf16(x)) of each scaled value
+// x, in the same order, so q_cat + q_lo carries about 16 significant bits of x.
+
+// Split plan of one decode call (see PlanArgs), built by one wave: lane l takes a
+// contiguous run of sequences, the wave scans the runs' totals, then every lane
+// writes its sequences' offsets and list entries.
+__device__ void build_plan(const PlanArgs& p, int l) {
+  const int per = (p.batch + 63) / 64;
+  const int b0 = min(p.batch, l * per), b1 = min(p.batch, b0 + per);
+  auto splits = [&](int b, int* kv_out) __attribute__((always_inline)) {
+    const int kv = min(max(p.kv_lens[b], 0), p.max_kv_len);
+    *kv_out = kv;
+    return kv >= p.n_q ? (kv + p.chunk - 1) / p.chunk : 0;
+  };
+  int tot = 0, nf = 0, np = 0;
+  for (int b = b0; b < b1; ++b) {
+    int kv;
+    const int ns = splits(b, &kv);
+    tot += ns;
+    if (kv < p.precise_below) np += ns;
+    else nf += ns;
+  }
+  // exclusive scans over the lanes
+  int it = tot, ifa = nf, ipr = np;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t0 = __shfl_up(it, d), t1 = __shfl_up(ifa, d), t2 = __shfl_up(ipr, d);
+    if (l >= d) {
+      it += t0;
+      ifa += t1;
+      ipr += t2;
+    }
+  }
+  int ot = it - tot, of = ifa - nf, op = ipr - np;
+  for (int b = b0; b < b1; ++b) {
+    int kv;
+    int ns = splits(b, &kv);
+    ns = max(0, min(ns, p.cap - ot));  // never past the partial buffers
+    p.seq_off[b] = min(ot, p.cap);
+    const bool prec = kv < p.precise_below;
+    WorkItem* dst = prec ? p.precise + op : p.fast + of;
+    for (int s = 0; s < ns; ++s) dst[s] = WorkItem{b, s, ot + s, kv};
+    ot += ns;
+    if (prec) op += ns;
+    else of += ns;
+  }
+  if (l == 63) {
+    p.seq_off[p.batch] = min(ot, p.cap);
+    p.counts[0] = min(of, p.cap);
+    p.counts[1] = min(op, p.cap);
+  }
 }
 
 // grid (ceil(h / 4), 8), 8 waves: group g of 4 heads (4g .. 4g + 3), block nb of 64
@@ -80,40 +124,40 @@ __device__ __forceinline__ int64_t qfrag_off(const QPrepArgs& a, int m, int i, i
 // fragment-shaped loads touch 32) and become MFMA fragments through the wave's own
 // LDS area, which then stages the result into 16-byte chunks of 8 columns. LDS
 // operations of one wave execute in order, so the area needs no barrier. The chunks
-// of the 4 heads at one (row, column chunk) are adjacent lanes of the fragment order
+// of the 4 heads at one (row, column chunk) are adjacent lanes of the block order
 // above; the 4 waves' pieces of a line meet in the L2 of this workgroup's XCD.
 //
 // Waves 4-7 (side work, concurrent with the product's loads): zero the output rows
 // m = nb (mod 8) of these heads and rotate their q_R. The rotation angle depends on
 // the row and the pair only: each half wave takes one row, lane k forms the sine and
-// cosine of pair k once, and the 4 heads' chunks fetch them by lane shuffles.
+// cosine of pair k once, and the 4 heads' chunks fetch them by lane shuffles. Wave 4
+// of workgroup (0, 0) first builds the split plan.
 constexpr int kQHeads = 4;
 constexpr int kQColBlocks = 8;
 
 __global__ __launch_bounds__(512) void qprep_kernel(QPrepArgs a) {
-  constexpr int kQnB = 256 + 16;  // row of a wave's area (q_nope row, or 64 result columns), padded
+  constexpr int kQnB = 256 + 16;  // row of a wave's area (q_nope row, or 64 result columns hi + lo), padded
   __shared__ __attribute__((aligned(16))) char s_area[kQHeads][32 * kQnB];
   const int g = blockIdx.x, nb = blockIdx.y;
   const int tid = threadIdx.x, l = tid % 64;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64);
   const int i0 = kQHeads * g;
   const int nh = min(kQHeads, a.h - i0);  // heads in this group
+  const bool lo_out = a.q_lo != nullptr;
 
-  // query row m -> its offset in the fragment order without the column part
-  // (qfrag_off(m, i, c) = row_off(m, i) + col_off(c))
+  // query row m, head i -> offset of the block-order element (m, i, column 0)
+  // (the column adds col_off(c))
   const int KS = (512 + a.d_r) / 16;
-  const int HG = a.rows_per_wg / a.n_q;
-  const int hgroups = a.h / HG, nwq = a.rows_per_wg / 32;
+  const int HB = a.h / 32;
   auto row_off = [&](int m, int i) __attribute__((always_inline)) -> int64_t {
-    const int b = a.n_q == 1 ? m : m / a.n_q, j = m - b * a.n_q;
-    const int hg = i / HG, r = j * HG + (i - hg * HG);
-    return ((((static_cast<int64_t>(b) * hgroups + hg) * nwq + (r >> 5)) * KS) * 64 + (r & 31)) * 8;
+    return ((static_cast<int64_t>(m) * HB + (i >> 5)) * KS * 64 + (i & 31)) * 8;
   };
   auto col_off = [](int c) __attribute__((always_inline)) -> int { return ((c >> 4) * 64 + 32 * ((c >> 3) & 1)) * 8 + (c & 7); };
 
   if (w >= kQHeads) {
     // ================= side work: waves 4-7 =================
     const int sw = w - kQHeads, st = tid - 64 * kQHeads;
+    if (g == 0 && nb == 0 && sw == 0) build_plan(a.plan, l);
     const int srows = a.M > nb ? (a.M - nb + kQColBlocks - 1) / kQColBlocks : 0;
     // RoPE of q_R: half wave hf of wave sw takes side row t = 8u + 2sw + hf (u = 0, 1, ..),
     // query row m = nb + 8t. Pair k (columns 2k, 2k + 1) turns by pos * inv_freq[k], the
@@ -138,16 +182,22 @@ __global__ __launch_bounds__(512) void qprep_kernel(QPrepArgs a) {
         const double red = theta - 6.283185307179586 * rint(theta * 0.15915494309189535);
         sincosf(static_cast<float>(red), &sn, &cs);
       }
-      u32x4 o;
+      u32x4 o, ol;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const int src = 32 * hf + ((4 * ch + p) & 31);  // every lane takes part
         const float c = __shfl(cs, src), sv = __shfl(sn, src);
         const float x0 = bf16_bits_to_f32(static_cast<uint16_t>(x[p] & 0xFFFFu));
         const float x1 = bf16_bits_to_f32(static_cast<uint16_t>(x[p] >> 16));
-        o[p] = pack_bf16x2((x0 * c - x1 * sv) * a.qscale, (x0 * sv + x1 * c) * a.qscale);
+        const float y0 = (x0 * c - x1 * sv) * a.qscale, y1 = (x0 * sv + x1 * c) * a.qscale;
+        o[p] = pack_bf16x2(y0, y1);
+        ol[p] = pack_bf16x2(y0 - __uint_as_float(o[p] << 16), y1 - __uint_as_float(o[p] & 0xFFFF0000u));
       }
-      if (item) *reinterpret_cast<u32x4*>(a.q_cat + row_off(m, i0 + hh) + col_off(512 + 8 * ch)) = o;
+      if (item) {
+        const int64_t off = row_off(m, i0 + hh) + col_off(512 + 8 * ch);
+        *reinterpret_cast<u32x4*>(a.q_cat + off) = o;
+        if (lo_out) *reinterpret_cast<u32x4*>(a.q_lo + off) = ol;
+      }
     }
     // zero the output rows m = nb (mod 8) of these heads (the combine adds into them)
     const int per_row = nh * 32;  // float4 per row of this head group
@@ -201,15 +251,23 @@ __global__ __launch_bounds__(512) void qprep_kernel(QPrepArgs a) {
         acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(bfr[cb][ks]), as_bf16x8(af[ks]), acc[cb], 0, 0, 0);
     }
     // stage in the area (its fragments are in registers): lane l holds row l%32 and
-    // columns 32cb + 8j + 4(l/32) + 0..3 in values 4j .. 4j+3
+    // columns 32cb + 8j + 4(l/32) + 0..3 in values 4j .. 4j+3; the high halves take
+    // bytes 0..127 of the row, the low halves (precise mode) bytes 128..255
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const f32x16& o = acc[cb];
-        const u32x2 v = {pack_bf16x2(o[4 * j] * a.qscale, o[4 * j + 1] * a.qscale),
-                         pack_bf16x2(o[4 * j + 2] * a.qscale, o[4 * j + 3] * a.qscale)};
-        *(lds_u32x2*)(lds_ptr(area) + (l & 31) * kQnB + (32 * cb + 8 * j + 4 * (l >> 5)) * 2) = v;
+        const float x0 = o[4 * j] * a.qscale, x1 = o[4 * j + 1] * a.qscale;
+        const float x2 = o[4 * j + 2] * a.qscale, x3 = o[4 * j + 3] * a.qscale;
+        const u32x2 v = {pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+        const int boff = (l & 31) * kQnB + (32 * cb + 8 * j + 4 * (l >> 5)) * 2;
+        *(lds_u32x2*)(lds_ptr(area) + boff) = v;
+        if (lo_out) {
+          const u32x2 vl = {pack_bf16x2(x0 - __uint_as_float(v[0] << 16), x1 - __uint_as_float(v[0] & 0xFFFF0000u)),
+                            pack_bf16x2(x2 - __uint_as_float(v[1] << 16), x3 - __uint_as_float(v[1] & 0xFFFF0000u))};
+          *(lds_u32x2*)(lds_ptr(area) + boff + 128) = vl;
+        }
       }
     // 32 rows x 8 chunks of 8 columns: chunk q = l + 64k -> row q/8, column chunk q%8
     const int cc = l & 7;
@@ -219,12 +277,16 @@ __global__ __launch_bounds__(512) void qprep_kernel(QPrepArgs a) {
       const int r = (l >> 3) + 8 * k, m = 32 * mb + r;
       const u32x4 v = *(lds_u32x4*)(lds_ptr(area) + r * kQnB + cc * 16);
       if (m < a.M && w < nh) *reinterpret_cast<u32x4*>(a.q_cat + row_off(m, hw) + coff) = v;
+      if (lo_out) {
+        const u32x4 vl = *(lds_u32x4*)(lds_ptr(area) + r * kQnB + 128 + cc * 16);
+        if (m < a.M && w < nh) *reinterpret_cast<u32x4*>(a.q_lo + row_off(m, hw) + coff) = vl;
+      }
     }
   }
 }
 
 hipError_t launch_qprep_bf16(const QPrepArgs& a, hipStream_t s) {
-  if (a.d_r % 8 != 0 || a.d_r > 64) return hipErrorInvalidValue;  // whole 16-byte q_R chunks
+  if (a.d_r % 8 != 0 || a.d_r > 64 || a.h % 32 != 0) return hipErrorInvalidValue;  // whole 16-byte q_R chunks
   qprep_kernel<<<dim3((a.h + kQHeads - 1) / kQHeads, kQColBlocks), 512, 0, s>>>(a);
   return hipGetLastError();
 }

@@ -67,6 +67,7 @@ class GpuStep:
         self.out = torch.empty((B, w.n_q, w.h * w.d_v), dtype=torch.float32, device=device)
         self.lse = torch.empty((B, w.n_q, w.h), dtype=torch.float32, device=device)
         self.workspace = None
+        self._ws_key = None
 
     def _append(self, t: dict):
         """Append every sequence's tokens 0 .. kv_len-1 (one call per sequence, since
@@ -107,10 +108,12 @@ class GpuStep:
                   kv_lens_host=self.kv_lens_host if use_host_lens else None,
                   gate_x=self.gate_x, w_gate=self.w_gate, num_splits=num_splits, events=events,
                   stream=stream)
-        if self.workspace is None or num_splits:
+        key = (num_splits, use_host_lens)
+        if self.workspace is None or key != self._ws_key:
             nbytes = self.workspace_bytes(num_splits, use_host_lens)
             if self.workspace is None or self.workspace.numel() < nbytes:
                 self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=self.device)
+            self._ws_key = key
         kw["workspace"] = self.workspace
         if w.paged:
             mla.mla_decode_paged(self.dims, self.pool, self.block_table, w.block_size, w.max_blocks,

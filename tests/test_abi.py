@@ -54,13 +54,86 @@ def call_decode(d, *, batch=32, n_q=1, max_kv_len=4097, t_max=4097, host=None, n
     return st, n.value
 
 
+PRECISE_BELOW = 4096   # sequences shorter than this take the precise attention form
+ALIGN = 256
+
+
+def cdiv(x, y):
+    return -(-x // y)
+
+
+def expected_workspace(*, h, n_q, batch, L, d_rope=64, host=None, num_splits=0, gated=False):
+    """The bf16 decode workspace, from the plan the library documents: token ranges
+    of `chunk` tokens (a multiple of 32), one (sequence, range) pair per range, fp32
+    partial rows of 512 plus (m, l) per pair x query row, the plan's lists and the
+    query blocks (a second, low-half copy when a short sequence may be present)."""
+    rows = h * n_q
+    fast_groups = rows // 128 if rows % 128 == 0 else rows // 64
+    prec_groups = rows // 64
+    groups = lambda kv: prec_groups if kv < PRECISE_BELOW else fast_groups
+    ragged = False
+    if host is not None:
+        total = sum(min(k, L) for k in host)
+        units = sum(min(k, L) * groups(min(k, L)) for k in host)
+        ragged = total * 5 < batch * L * 4
+    if num_splits:
+        chunk = cdiv(L, num_splits)
+    elif ragged:
+        chunk = max(256, cdiv(units, 3 * 256))
+    else:
+        chunk = cdiv(L, min(cdiv(256, batch * groups(L)), cdiv(L, 32)))
+    chunk = max(chunk, cdiv(L, 1024))
+    chunk = min(cdiv(chunk, 32) * 32, cdiv(L, 32) * 32)
+    if host is not None:
+        ns = [cdiv(min(k, L), chunk) if k >= n_q else 0 for k in host]
+        cap = sum(ns)
+        prec = sum(n for n, k in zip(ns, host) if min(k, L) < PRECISE_BELOW)
+    else:
+        cap = batch * cdiv(L, chunk)
+        prec = cap
+    al = lambda x: cdiv(x, ALIGN) * ALIGN
+    M = batch * n_q
+    q = al(M * h * (512 + d_rope) * 2)
+    n = al(8) + al((batch + 1) * 4) + 2 * al(max(cap, 1) * 16) + q + (q if prec else 0)
+    n += al(max(cap, 1) * n_q * h * 512 * 4) + al(max(cap, 1) * n_q * h * 8)
+    if gated:
+        n += al(16 * M * h * 128 * 4)
+    return n, chunk, cap
+
+
 def test_workspace_query_deepseek_shape():
     st, n = call_decode(ds_dims())
     assert st == mla.MLA_OK
-    # q_cat + 8 splits of bf16 partial rows and fp32 (m, l) per (sequence, head)
-    q_cat = 32 * 128 * 576 * 2
-    parts = 32 * 8 * 128 * (512 * 2 + 2 * 4)
-    assert q_cat + parts <= n <= q_cat + parts + 3 * 256
+    # without host lengths any sequence may be short: the low query halves are kept
+    exp, chunk, cap = expected_workspace(h=128, n_q=1, batch=32, L=4097)
+    assert (chunk, cap) == (544, 256) and n == exp
+    # with host lengths of 4097 every sequence takes the fast form: no low halves
+    st, n2 = call_decode(ds_dims(), host=[4097] * 32)
+    assert st == mla.MLA_OK and n2 == expected_workspace(h=128, n_q=1, batch=32, L=4097, host=[4097] * 32)[0]
+    assert n - n2 == 32 * 128 * 576 * 2
+
+
+def test_one_long_many_short_batch_plans_compactly():
+    """One 65537-token sequence and fifteen 101-token ones: the partials of each
+    sequence take only its own ranges (no [batch][max ranges] layout), so the
+    workspace stays near the cache's size instead of growing with batch x ranges."""
+    host = [65537] + [101] * 15
+    st, n = call_decode(ds_dims(), batch=16, max_kv_len=65537, t_max=65537, host=host)
+    assert st == mla.MLA_OK
+    exp, chunk, cap = expected_workspace(h=128, n_q=1, batch=16, L=65537, host=host)
+    assert n == exp
+    assert cap == cdiv(65537, chunk) + 15 * cdiv(101, chunk)
+    cache = sum(host) * 576 * 2
+    assert n < 1.5 * cache
+    # one long sequence + thirty-one 600-token ones
+    host = [32769] + [600] * 31
+    st, n = call_decode(ds_dims(), batch=32, max_kv_len=32769, t_max=32769, host=host)
+    assert st == mla.MLA_OK and n == expected_workspace(h=128, n_q=1, batch=32, L=32769, host=host)[0]
+    # forced split counts far past what a 128-row group could hold before
+    for ns in (192, 400, 1024):
+        st, n = call_decode(ds_dims(), num_splits=ns, max_kv_len=32769, t_max=32769)
+        assert st == mla.MLA_OK
+        assert n == expected_workspace(h=128, n_q=1, batch=32, L=32769, num_splits=ns)[0]
 
 
 def test_rejections_happen_on_the_host():
@@ -73,6 +146,9 @@ def test_rejections_happen_on_the_host():
     assert call_decode(ds_dims(), host=[4097] * 31 + [5000])[0] == mla.MLA_E_SHAPE
     assert call_decode(ds_dims(), host=[0] + [4097] * 31)[0] == mla.MLA_E_SHAPE  # kv_len < n_q
     assert call_decode(ds_dims(n_heads=96))[0] == mla.MLA_E_UNSUPPORTED       # 96 rows per step
+    assert call_decode(ds_dims(n_heads=48), n_q=4)[0] == mla.MLA_E_UNSUPPORTED  # heads in 32-head blocks
+    assert call_decode(ds_dims(n_heads=96), n_q=2)[0] == mla.MLA_OK             # 3 x 64-row groups
+    assert call_decode(ds_dims(n_heads=64), n_q=3)[0] == mla.MLA_OK             # 192 rows
     assert call_decode(ds_dims(n_heads=64), batch=16)[0] == mla.MLA_OK             # 64-row groups, with RoPE
     assert call_decode(ds_dims(n_heads=64, d_rope=0), batch=16)[0] == mla.MLA_OK
     assert call_decode(ds_dims(), num_splits=-1)[0] == mla.MLA_E_SHAPE
@@ -112,14 +188,11 @@ def test_split_plan_sizes():
     """Ranges are multiples of 32 tokens and cover max_kv_len."""
     d = ds_dims()
     for L in (33, 4097, 32769):
-        for s in (1, 2, 7, 64):
-            st, n = call_decode(d, batch=4, max_kv_len=L, t_max=L, num_splits=s)
+        for ns in (1, 2, 7, 64):
+            st, n = call_decode(d, batch=4, max_kv_len=L, t_max=L, num_splits=ns)
             assert st == mla.MLA_OK
-            chunk = -(-(-(-L // s)) // 32) * 32
-            splits = -(-L // chunk)
-            q_cat = 4 * 128 * 576 * 2
-            parts = 4 * splits * 128 * (512 * 2 + 2 * 4)
-            assert q_cat + parts <= n <= q_cat + parts + 3 * 256
+            exp, chunk, cap = expected_workspace(h=128, n_q=1, batch=4, L=L, num_splits=ns)
+            assert n == exp and chunk % 32 == 0 and cap == 4 * cdiv(L, chunk)
 
 
 def test_split_plan_64_row_groups():
@@ -127,14 +200,11 @@ def test_split_plan_64_row_groups():
     sequence gets 256 / batch token ranges, each holding 64 partial rows."""
     for d_rope in (64, 0):
         d = ds_dims(n_heads=64, d_rope=d_rope)
-        st, n = call_decode(d, batch=16, max_kv_len=65537, t_max=65537)
+        host = [65537] * 16
+        st, n = call_decode(d, batch=16, max_kv_len=65537, t_max=65537, host=host)
         assert st == mla.MLA_OK
-        chunk = -(-(-(-65537 // 16)) // 32) * 32
-        splits = -(-65537 // chunk)
-        assert splits == 16
-        q_cat = 16 * 64 * (512 + d_rope) * 2
-        parts = 16 * splits * 64 * (512 * 2 + 2 * 4)
-        assert q_cat + parts <= n <= q_cat + parts + 3 * 256
+        exp, chunk, cap = expected_workspace(h=64, n_q=1, batch=16, L=65537, d_rope=d_rope, host=host)
+        assert n == exp and cap == 16 * 16
 
 
 def call_project(d, *, batch=32, n_new=1, d_model=4096, ws=None, ws_bytes=0, k_splits=0, eps=1e-6,
