@@ -19,10 +19,12 @@ namespace {
 constexpr int kGateSplit = 16;             // K-splits of the gate GEMM
 constexpr int kHalf = 256;                 // latent columns per workgroup (half of d_c)
 constexpr int kAStride = kHalf * 2 + 16;   // bytes per o_lat half row in LDS (padded)
-constexpr int kBatch = 8;                  // partial half rows loaded per wave before merging
+constexpr int kBatch = 8;                  // partial half rows per row in flight at once
+constexpr int kWaves = 8;                  // waves per workgroup
+constexpr int kRowsPerWave = 4;            // query rows per wave (32 per workgroup)
 }  // namespace
 
-// grid (h, 2, ceil(M / R)), 256 threads, R <= 32 query rows per workgroup. Workgroup
+// grid (h, 2, ceil(M / R)), 512 threads, R <= 32 query rows per workgroup. Workgroup
 // (i, kh, mb) takes head i, latent columns [256 kh, 256 kh + 256) and query rows
 // m0 .. m0 + R - 1, and adds its share of the up-projection,
 //   out[m][i*128 + d] += Σ_{c in half kh} o_lat[m][i][c] · W_UV_i[c][d],
@@ -32,67 +34,98 @@ constexpr int kBatch = 8;                  // partial half rows loaded per wave 
 // reads each partial row and each W_UV_i once.
 //
 // Sequence b's ranges hold partial indices seq_off[b] .. seq_off[b + 1] - 1 (the
-// plan's compact layout). Wave w takes rows w, w + 4, ...: first the statistics of
-// each row (lanes over ranges, wave reductions), then the merge of its half row,
-// lane l holding columns 4l .. 4l + 3: the range loads go out eight at a time, and
-// lane k < 8 of a batch forms range k's weight 2^(m_s - M) / L, which the wave reads
-// back with readlane. Ranges merge in a fixed order, so the result is deterministic.
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+// plan's compact layout). Wave w takes rows w, w + 8, w + 16, w + 24, lane l columns
+// 4l .. 4l + 3 of the half row. Everything a wave needs goes out at once: the (m, l)
+// of each row's first 64 ranges (lane s: range s) and the half rows of its first 8
+// ranges, so a wave waits for memory about once. Lane s then forms range s's weight
+// 2^(m_s - M) / L, which the merge reads back with readlane; further ranges come 8
+// at a time. Ranges merge in a fixed order, so the result is deterministic. Waves
+// 0-3 also load the W_UV_i fragments first and run the up-projection.
+__global__ __launch_bounds__(kWaves * 64) void combine_kernel(CombineArgs a) {
   __shared__ __attribute__((aligned(16))) char s_hi[32 * kAStride];
   __shared__ __attribute__((aligned(16))) char s_lo[32 * kAStride];
   const int i = blockIdx.x, kh = blockIdx.y, mb = blockIdx.z;
   const int tid = threadIdx.x, l = tid % 64;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64);
   const int M = a.batch * a.n_q;
-  const int R = a.rows_per_wg;
-  const int m0 = mb * R;
-  const int rows = min(R, M - m0);
+  const int m0 = mb * a.rows_per_wg;
+  const int rows = min(a.rows_per_wg, M - m0);
+  const int64_t rstride = static_cast<int64_t>(a.n_q) * a.h;  // partial rows per range
 
-  // W_UV_i fragments of this wave's 32 output columns, 16 k-steps of half kh: issued
-  // first, used last
-  const u32x4* wv = reinterpret_cast<const u32x4*>(a.w_uv_pk) + ((static_cast<int64_t>(i) * 4 + w) * 32 + 16 * kh) * 64 + l;
+  // W_UV_i fragments of wave w's 32 output columns, 16 k-steps of half kh
   u32x4 bfr[16];
+  if (w < 4) {
+    const u32x4* wv = reinterpret_cast<const u32x4*>(a.w_uv_pk) + ((static_cast<int64_t>(i) * 4 + w) * 32 + 16 * kh) * 64 + l;
 #pragma unroll
-  for (int ks = 0; ks < 16; ++ks) bfr[ks] = wv[ks * 64];
+    for (int ks = 0; ks < 16; ++ks) bfr[ks] = wv[ks * 64];
+  }
 
-#pragma unroll 1
-  for (int k = 0; k < 8; ++k) {
-    const int r = w + 4 * k;  // uniform
+  // this wave's rows: (first partial row, number of ranges)
+  int64_t row0[kRowsPerWave];
+  int ns[kRowsPerWave];
+#pragma unroll
+  for (int k = 0; k < kRowsPerWave; ++k) {
+    const int r = w + kWaves * k;
+    ns[k] = 0;
+    row0[k] = 0;
+    if (r < rows) {  // uniform
+      const int m = m0 + r, b = m / a.n_q, j = m - b * a.n_q;
+      const int p0 = a.seq_off[b];
+      ns[k] = a.seq_off[b + 1] - p0;
+      row0[k] = (static_cast<int64_t>(p0) * a.n_q + j) * a.h + i;
+    }
+  }
+  // (m, l) of ranges l (< 64) and the first kBatch half rows of every row
+  f32x2 ml[kRowsPerWave];
+  f32x4 v[kRowsPerWave][kBatch];
+#pragma unroll
+  for (int k = 0; k < kRowsPerWave; ++k) {
+    ml[k] = l < ns[k] ? *reinterpret_cast<const f32x2*>(a.ml_part + (row0[k] + l * rstride) * 2)
+                      : f32x2{-INFINITY, 0.f};
+    const float* src = a.o_part + row0[k] * 512 + kHalf * kh + 4 * l;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      v[k][u] = u < ns[k] ? *reinterpret_cast<const f32x4*>(src + u * rstride * 512) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+#pragma unroll
+  for (int k = 0; k < kRowsPerWave; ++k) {
+    const int r = w + kWaves * k;
     if (r >= 32) break;
     u32x2 hv = {0u, 0u}, lv = {0u, 0u};
-    if (r < rows) {
-      const int m = m0 + r, b = m / a.n_q, j = m - b * a.n_q;
-      const int p0 = a.seq_off[b], ns = a.seq_off[b + 1] - p0;
-      // row index of range s of this (query, head) row: (p0 + s) * n_q + j, head i
-      const int64_t row0 = (static_cast<int64_t>(p0) * a.n_q + j) * a.h + i;
-      const int64_t rstride = static_cast<int64_t>(a.n_q) * a.h;
-      // ---- statistics: M and L over the ranges (lanes over ranges)
-      float mx = -INFINITY;
-      for (int s = l; s < ns; s += 64) mx = fmaxf(mx, a.ml_part[(row0 + s * rstride) * 2]);
+    if (r < rows) {  // uniform
+      // ---- statistics over the ranges (ranges past 64 in a loop)
+      float mx = ml[k][0];
+      for (int s = l + 64; s < ns[k]; s += 64) mx = fmaxf(mx, a.ml_part[(row0[k] + s * rstride) * 2]);
       mx = wave_max(mx);
       const float mref = mx == -INFINITY ? 0.f : mx;
-      float L = 0.f;
-      for (int s = l; s < ns; s += 64) {
-        const f32x2 v = *reinterpret_cast<const f32x2*>(a.ml_part + (row0 + s * rstride) * 2);
-        L += fast_exp2(v[0] - mref) * v[1];
+      float L = l < ns[k] ? fast_exp2(ml[k][0] - mref) * ml[k][1] : 0.f;
+      for (int s = l + 64; s < ns[k]; s += 64) {
+        const f32x2 q = *reinterpret_cast<const f32x2*>(a.ml_part + (row0[k] + s * rstride) * 2);
+        L += fast_exp2(q[0] - mref) * q[1];
       }
       L = wave_sum(L);
       const float inv_l = L > 0.f ? 1.f / L : 0.f;
-      if (kh == 0 && a.lse && l == 0) a.lse[static_cast<int64_t>(m) * a.h + i] = L > 0.f ? (mx + __log2f(L)) * kLn2 : -INFINITY;
+      if (kh == 0 && a.lse && l == 0) a.lse[static_cast<int64_t>(m0 + r) * a.h + i] = L > 0.f ? (mx + __log2f(L)) * kLn2 : -INFINITY;
       // ---- merge: o = Σ_s 2^(m_s - M) / L · O_s over this lane's 4 columns
+      const float wl = l < ns[k] ? fast_exp2(ml[k][0] - mref) * inv_l : 0.f;  // weight of range l
       f32x4 o = {0.f, 0.f, 0.f, 0.f};
-      const float* src = a.o_part + row0 * 512 + kHalf * kh + 4 * l;
-      for (int s0 = 0; s0 < ns; s0 += kBatch) {  // uniform
-        f32x4 v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) o += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u)) * v[k][u];
+      const float* src = a.o_part + row0[k] * 512 + kHalf * kh + 4 * l;
+      for (int s0 = kBatch; s0 < ns[k]; s0 += kBatch) {  // uniform: rows with more than 8 ranges
+        f32x4 q[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u)
-          v[u] = s0 + u < ns ? *reinterpret_cast<const f32x4*>(src + (s0 + u) * rstride * 512) : f32x4{0.f, 0.f, 0.f, 0.f};
-        float wl = 0.f;
-        if (l < kBatch && s0 + l < ns) wl = fast_exp2(a.ml_part[(row0 + (s0 + l) * rstride) * 2] - mref) * inv_l;
+          q[u] = s0 + u < ns[k] ? *reinterpret_cast<const f32x4*>(src + (s0 + u) * rstride * 512) : f32x4{0.f, 0.f, 0.f, 0.f};
+        float wb = 0.f;  // lane u < kBatch: weight of range s0 + u past the first 64
+        if (s0 >= 64 && l < kBatch && s0 + l < ns[k])
+          wb = fast_exp2(a.ml_part[(row0[k] + (s0 + l) * rstride) * 2] - mref) * inv_l;
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-          const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u));
-          o += wu * v[u];
+          const float wu = s0 < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), s0 + u))
+                                   : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wb), u));
+          o += wu * q[u];
         }
       }
       // o_lat as a hi + lo pair of bf16 (hi = bf16(o), lo = bf16(o - hi))
@@ -105,6 +138,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     *(lds_u32x2*)(lds_ptr(s_lo) + r * kAStride + l * 8) = lv;
   }
   __syncthreads();
+  if (w >= 4) return;
 
   // ---- out[m][i*128 + 32w + ..] += (o_hi + o_lo)[m][half kh] · W_UV_i[half kh][32w + ..]
   f32x16 acc = {};
@@ -135,9 +169,9 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 
 hipError_t launch_combine_bf16(const CombineArgs& a, hipStream_t s) {
   const int M = a.batch * a.n_q;
-  if (a.rows_per_wg < 1 || a.rows_per_wg > 32 || M <= 0) return hipErrorInvalidValue;
+  if (a.rows_per_wg < 1 || a.rows_per_wg > kWaves * kRowsPerWave || M <= 0) return hipErrorInvalidValue;
   const dim3 grid(a.h, 2, (M + a.rows_per_wg - 1) / a.rows_per_wg);
-  combine_kernel<<<grid, 256, 0, s>>>(a);
+  combine_kernel<<<grid, kWaves * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 

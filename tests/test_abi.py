@@ -68,7 +68,12 @@ def expected_workspace(*, h, n_q, batch, L, d_rope=64, host=None, num_splits=0, 
     partial rows of 512 plus (m, l) per pair x query row, the plan's lists and the
     query blocks (a second, low-half copy when a short sequence may be present)."""
     rows = h * n_q
-    fast_groups = rows // 128 if rows % 128 == 0 else rows // 64
+    fast_groups = rows // 64   # the role-split form, unless 128-row ranges would be long
+    if rows % 128 == 0:
+        units = batch * (rows // 128)
+        c128 = cdiv(L, min(cdiv(256, units), cdiv(L, 32)))
+        if num_splits or c128 >= 1024:
+            fast_groups = rows // 128
     prec_groups = rows // 64
     groups = lambda kv: prec_groups if kv < PRECISE_BELOW else fast_groups
     ragged = False
@@ -106,7 +111,7 @@ def test_workspace_query_deepseek_shape():
     assert st == mla.MLA_OK
     # without host lengths any sequence may be short: the low query halves are kept
     exp, chunk, cap = expected_workspace(h=128, n_q=1, batch=32, L=4097)
-    assert (chunk, cap) == (544, 256) and n == exp
+    assert (chunk, cap) == (1056, 128) and n == exp  # 64-row groups: 4 ranges per sequence
     # with host lengths of 4097 every sequence takes the fast form: no low halves
     st, n2 = call_decode(ds_dims(), host=[4097] * 32)
     assert st == mla.MLA_OK and n2 == expected_workspace(h=128, n_q=1, batch=32, L=4097, host=[4097] * 32)[0]
