@@ -165,6 +165,26 @@ mla_status mla_decode_paged(const mla_dims* dims, const void* pool, const int32_
                             const mla_decode_args* args, hipStream_t stream);
 
 /*
+ * Allocation-free decode, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and kernels as mla_decode / mla_decode_paged, with the
+ * workspace taken from a 64 MiB array that the library holds on each GPU it runs
+ * on (from its first use on that GPU until the process ends) instead of from the
+ * caller. `layout` selects the cache form as for mla_append_latent: contiguous
+ * [batch][t_max][row] when layout->block_table is NULL, else the paged pool with
+ * block_size a multiple of 32. args->workspace and args->workspace_bytes are
+ * ignored. MLA_E_WORKSPACE if the call would need more than 64 MiB of workspace
+ * (the DeepSeek-shaped step, 32 sequences of 4097 tokens, needs about 43 MB).
+ * The call allocates and frees nothing and clears nothing: every call rewrites the
+ * parts of the array it reads. All calls on one GPU share its array, so calls that
+ * overlap on one GPU (on different streams, or from different threads without
+ * ordering) race and their results are undefined; calls ordered on one stream are
+ * safe.
+ */
+mla_status mla_decode_noalloc(const mla_dims* dims, const void* cache, const mla_cache_layout* layout,
+                              const mla_decode_args* args, hipStream_t stream);
+
+/*
  * Fused latent append from the hidden state: the cache row of each new token,
  *   [ gain ⊙ c / sqrt(mean(c²) + eps)  ‖  RoPE(h · W_KR, pos) ],  c = h · W_DKV,
  * computed and stored in one call (tutorial §2.2: c_KV = h · W_DKV with W_DKV of

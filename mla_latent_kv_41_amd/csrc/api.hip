@@ -6,11 +6,19 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "mla.h"
 #include "launch.hpp"
 
 using namespace mla;
+
+// The allocation-free decode's workspace: one array on each GPU the library runs
+// on, held until the process ends. kScratchBytes covers the DeepSeek-shaped step
+// (32 sequences of 4097 tokens: about 43 MB without host lengths) and anything that
+// needs as much workspace.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
 
 namespace {
 
@@ -366,6 +374,26 @@ mla_status decode_impl(const mla_dims* dims, const CacheRef& cache, const mla_de
   return launch_combine_bf16(c, stream) == hipSuccess ? MLA_OK : MLA_E_HIP;
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};  // the array's device address on each GPU, once looked up
+
+// The current device's copy of `scratch`. The host-side name of the array is not a
+// device address: host code only ever passes on the address looked up here, once per
+// device, with that device current.
+mla_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MLA_E_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -437,6 +465,34 @@ mla_status mla_decode_paged(const mla_dims* dims, const void* pool, const int32_
   if (args && args->workspace && !block_table) return MLA_E_NULL;
   CacheRef c{pool, block_table, 0, block_size, max_blocks, n_blocks};
   return decode_impl(dims, c, args, stream);
+}
+
+mla_status mla_decode_noalloc(const mla_dims* dims, const void* cache, const mla_cache_layout* layout,
+                              const mla_decode_args* args, hipStream_t stream) {
+  if (!layout || !args) return MLA_E_NULL;
+  CacheRef c{cache, layout->block_table, layout->t_max, layout->block_size, layout->max_blocks, layout->n_blocks};
+  if (layout->block_table) {
+    if (layout->block_size <= 0 || layout->block_size % kTile != 0 || layout->max_blocks <= 0 || layout->n_blocks <= 0)
+      return MLA_E_SHAPE;
+    if (static_cast<int64_t>(layout->max_blocks) * layout->block_size < args->max_kv_len) return MLA_E_SHAPE;
+  } else if (layout->t_max <= 0 || layout->t_max < args->max_kv_len) {
+    return MLA_E_SHAPE;
+  }
+  // the workspace this call needs, on the host; then the same call on the scratch array
+  mla_decode_args la = *args;
+  size_t need = 0;
+  la.workspace = nullptr;
+  la.workspace_bytes = &need;
+  mla_status st = decode_impl(dims, c, &la, stream);
+  if (st != MLA_OK) return st;
+  if (need > kScratchBytes) return MLA_E_WORKSPACE;  // past the library's scratch
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != MLA_OK) return st;
+  size_t have = kScratchBytes;
+  la.workspace = ws;
+  la.workspace_bytes = &have;
+  return decode_impl(dims, c, &la, stream);
 }
 
 mla_status mla_pack_down_weights(const mla_dims* dims, int32_t d_model, const void* w_dkv, const void* w_kr,

@@ -18,7 +18,7 @@ MLA_OK, MLA_E_NULL, MLA_E_SHAPE, MLA_E_DTYPE, MLA_E_UNSUPPORTED, MLA_E_WORKSPACE
 MLA_F32, MLA_BF16 = 0, 1
 
 EXPORTS = ("mla_absorb_weights", "mla_append_latent", "mla_decode", "mla_decode_paged",
-           "mla_pack_down_weights", "mla_project_append", "mla_status_string")
+           "mla_decode_noalloc", "mla_pack_down_weights", "mla_project_append", "mla_status_string")
 
 
 class MLAError(RuntimeError):
@@ -84,6 +84,9 @@ def lib():
         L.mla_decode_paged.restype = st
         L.mla_decode_paged.argtypes = [ctypes.POINTER(mla_dims), vp, vp, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.POINTER(mla_decode_args), vp]
+        L.mla_decode_noalloc.restype = st
+        L.mla_decode_noalloc.argtypes = [ctypes.POINTER(mla_dims), vp, ctypes.POINTER(mla_cache_layout),
+                                         ctypes.POINTER(mla_decode_args), vp]
         L.mla_pack_down_weights.restype = st
         L.mla_pack_down_weights.argtypes = [ctypes.POINTER(mla_dims), ctypes.c_int32, vp, vp, vp,
                                             ctypes.POINTER(ctypes.c_size_t), vp]
@@ -310,6 +313,22 @@ def mla_decode_paged(d: mla_dims, pool, block_table, block_size: int, max_blocks
     return _check(lib().mla_decode_paged(ctypes.byref(d), _ptr(pool), _ptr(block_table), block_size,
                                          max_blocks, n_blocks, ctypes.byref(a), _stream(stream)),
                   "mla_decode_paged")
+
+
+def mla_decode_noalloc(d: mla_dims, cache, *, kv_lens, max_kv_len: int, q_nope, q_rope, packed_w, out,
+                       t_max: int = 0, block_table=None, block_size: int = 0, max_blocks: int = 0,
+                       n_blocks: int = 0, kv_lens_host: Optional[Sequence[int]] = None, gate_x=None,
+                       w_gate=None, lse=None, num_splits: int = 0, events=None, stream=None) -> int:
+    """Decode with the library's own per-GPU scratch array as the workspace (no
+    workspace argument; contiguous cache when block_table is None, else paged)."""
+    B, n_q = q_nope.shape[0], q_nope.shape[1]
+    layout = mla_cache_layout(_ptr(block_table), t_max, block_size, max_blocks, n_blocks)
+    a, n, _h = _decode_args(batch=B, n_q=n_q, kv_lens=kv_lens, kv_lens_host=kv_lens_host,
+                            max_kv_len=max_kv_len, q_nope=q_nope, q_rope=q_rope, packed_w=packed_w,
+                            gate_x=gate_x, w_gate=w_gate, out=out, lse=lse, workspace=None,
+                            workspace_bytes=0, num_splits=num_splits, events=events)
+    return _check(lib().mla_decode_noalloc(ctypes.byref(d), _ptr(cache), ctypes.byref(layout), ctypes.byref(a),
+                                           _stream(stream)), "mla_decode_noalloc")
 
 
 def decode_workspace_bytes(d: mla_dims, *, batch: int, n_q: int, max_kv_len: int,

@@ -255,3 +255,26 @@ def test_fused_append_sizes_and_rejections():
     assert mla.lib().mla_pack_down_weights(ctypes.byref(d), 64, None, None, 1, ctypes.byref(n), None) == mla.MLA_E_WORKSPACE
     n.value = 64 * 576 * 2
     assert mla.lib().mla_pack_down_weights(ctypes.byref(d), 64, None, None, 1, ctypes.byref(n), None) == mla.MLA_E_NULL
+
+
+def test_noalloc_host_checks():
+    """The allocation-free decode validates its layout and the workspace it would
+    need on the host: a call past its 64 MiB scratch is refused before any device
+    call."""
+    d = ds_dims()
+    a, n, _h = mla._decode_args(batch=64, n_q=1, kv_lens=None, kv_lens_host=None, max_kv_len=65537,
+                                q_nope=None, q_rope=None, packed_w=None, gate_x=None, w_gate=None,
+                                out=None, lse=None, workspace=None, workspace_bytes=0, num_splits=0,
+                                events=None)
+    L = mla.lib()
+    lay = mla.mla_cache_layout(None, 65537, 0, 0, 0)
+    assert L.mla_decode_noalloc(ctypes.byref(d), None, None, ctypes.byref(a), None) == mla.MLA_E_NULL
+    assert L.mla_decode_noalloc(ctypes.byref(d), None, ctypes.byref(lay), None, None) == mla.MLA_E_NULL
+    assert L.mla_decode_noalloc(ctypes.byref(d), None, ctypes.byref(lay), ctypes.byref(a), None) == mla.MLA_E_WORKSPACE
+    short = mla.mla_cache_layout(None, 100, 0, 0, 0)   # cache shorter than max_kv_len
+    assert L.mla_decode_noalloc(ctypes.byref(d), None, ctypes.byref(short), ctypes.byref(a), None) == mla.MLA_E_SHAPE
+    paged = mla.mla_cache_layout(1, 0, 48, 2000, 4000)  # block size not a multiple of 32
+    assert L.mla_decode_noalloc(ctypes.byref(d), None, ctypes.byref(paged), ctypes.byref(a), None) == mla.MLA_E_SHAPE
+    # the DeepSeek-shaped step fits: its workspace is well under 64 MiB
+    st, need = call_decode(d)
+    assert st == mla.MLA_OK and need < 64 << 20

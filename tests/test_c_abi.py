@@ -40,6 +40,10 @@ int main(void) {
   p.d_model = 100;
   printf("project_bad %d\n", (int)mla_project_append(&d, NULL, &lay, &p, 0));
 
+  mla_cache_layout big = {NULL, 65537, 0, 0, 0};
+  a.batch = 64; a.max_kv_len = 65537; a.workspace_bytes = NULL;
+  printf("noalloc_big %d\n", (int)mla_decode_noalloc(&d, NULL, &big, &a, 0));
+
   printf("status %s\n", mla_status_string(MLA_E_WORKSPACE));
   return 0;
 }
@@ -73,4 +77,5 @@ def test_c_program_uses_the_abi(c_program):
     assert int(out["pack_down"]) == 4096 * 576 * 2
     assert int(out["project_ws"]) == mla.project_workspace_bytes(d, batch=32, n_new=1, d_model=4096)
     assert int(out["project_bad"]) == mla.MLA_E_UNSUPPORTED
+    assert int(out["noalloc_big"]) == mla.MLA_E_WORKSPACE
     assert out["status"] == mla.status_string(mla.MLA_E_WORKSPACE)
