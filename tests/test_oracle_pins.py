@@ -475,3 +475,35 @@ def test_project_latent_gain_and_scale_invariants():
     a, b = run_project(w, t, eps=0.0), run_project(w, t4, eps=0.0)
     np.testing.assert_allclose(b[:, :w.d_c], a[:, :w.d_c], rtol=1e-14, atol=1e-15)
     np.testing.assert_allclose(b[:, w.d_c:], 4.0 * a[:, w.d_c:], rtol=1e-14, atol=1e-14)
+
+
+def _count_explicit_ops(h, d_c, d_n, d_v, d_r, kv_lens, n_q, d_model):
+    """Floating-point operations of the explicit-K/V definition, counted one
+    multiply-add (2 operations) at a time while walking its loops: K and V of every
+    cached token of every (sequence, head), then each query's scores over the visible
+    tokens and its weighted sum of values, then the gate's logits."""
+    ops = 0
+    for n in kv_lens:
+        for _i in range(h):
+            for _t in range(n):
+                for _c in range(d_c):
+                    ops += 2 * d_n      # K[t] += c_t[c] * W_UK[c, :]
+                    ops += 2 * d_v      # V[t] += c_t[c] * W_UV[c, :]
+            for j in range(n_q):
+                vis = n - n_q + j + 1
+                for _t in range(vis):
+                    ops += 2 * (d_n + d_r)  # score
+                    ops += 2 * d_v          # p_t * V[t]
+                ops += 2 * d_v * d_model    # the gate's logits of this head's channels
+    return ops
+
+
+def test_unabsorbed_flops_counts_what_the_definition_executes():
+    """oracle.unabsorbed_flops (what the explicit form's CPU time is priced in)
+    equals a loop-by-loop count of the definition, and the tiny workload's count
+    done by hand: 2*4*65*32*(16+16) + 2*4*65*(16+8+16) = 532480 + 20800."""
+    assert oracle.unabsorbed_flops(4, 32, 16, 16, 8, [65], 1) == 553280
+    cases = [(4, 32, 16, 16, 8, [65], 1, 0), (2, 8, 4, 6, 2, [5, 9, 3], 2, 0), (3, 4, 2, 2, 0, [4, 6], 1, 5)]
+    for h, d_c, d_n, d_v, d_r, kv, n_q, dm in cases:
+        assert oracle.unabsorbed_flops(h, d_c, d_n, d_v, d_r, kv, n_q, d_model=dm) == \
+            _count_explicit_ops(h, d_c, d_n, d_v, d_r, kv, n_q, dm)
