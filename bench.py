@@ -353,7 +353,6 @@ def summarize_profiles(d):
     if not os.path.isdir(os.path.join(d, "prof_ds")):
         return
     w_name = "deepseek_b32_ctx4096"
-    kname = "mla::decode_kernel<4, 64>"
     shas = {_bench_line(os.path.join(d, "prof_ds.log"))["attention_kernel_source_sha256"]}
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         shas.add(_bench_line(os.path.join(d, "pmc", c + ".log"))["attention_kernel_source_sha256"])
@@ -366,12 +365,16 @@ def summarize_profiles(d):
         return name.split("(")[0] if not name.startswith("at::") else name.split(")")[0] + ")"
 
     stats = list(csv.DictReader(open(glob.glob(os.path.join(d, "prof_ds", "*kernel_stats.csv"))[0])))
+    attn = [short(r["Name"]) for r in stats if short(r["Name"]).startswith(ATTENTION_KERNELS)]
+    if len(attn) != 1:
+        raise SystemExit("expected one attention kernel in the DeepSeek-shaped trace, found %s" % attn)
+    kname = attn[0]
     lines = ["# Kernel trace: DeepSeek-shaped decode (h=128, B=32, 4096+1 tokens)", "",
              "Command (from /tmp with TMPDIR=/tmp; the run includes the bench's clock-settling steps):",
              "", "    " + TRACE_CMD, "",
-             "Per-step kernels: qprep_kernel (query absorption + RoPE, output zeroing), "
-             "decode_kernel<4,64> (split-K attention), combine_kernel (split merge + W_UV). "
-             "append_kernel, pack_kernel and the fills belong to set-up.", "",
+             "Per-step kernels: qprep_kernel (query absorption + RoPE, output zeroing, the split plan), "
+             "%s (split-K attention), combine_kernel (split merge + W_UV). "
+             "append_kernel, pack_kernel and the fills belong to set-up." % kname, "",
              "| kernel | calls | average us | min us | max us | share |", "|---|---|---|---|---|---|"]
     for r in stats:
         lines.append("| `%s` | %s | %.2f | %.2f | %.2f | %.1f%% |" % (
@@ -398,7 +401,7 @@ def summarize_profiles(d):
     dv = {c: sum(v) / len(v) for c, v in vals[dec[0]].items()}
     fetch_b = dv["FETCH_SIZE"] * 1024 * f_fac
     write_b = dv["WRITE_SIZE"] * 1024 * w_fac
-    lines = ["# HBM traffic counters: decode_kernel<4,64>, DeepSeek-shaped decode (h=128, B=32, 4096+1 tokens)", "",
+    lines = ["# HBM traffic counters: %s, DeepSeek-shaped decode (h=128, B=32, 4096+1 tokens)" % kname, "",
              "Commands (one counter per pass, from /tmp with TMPDIR=/tmp; `--calibrate-copy` adds one 512 MiB "
              "device-to-device copy, dispatched as `__amd_rocclr_copyBuffer` with grid %d):" % (COPY_BYTES // 4096), ""]
     lines += ["    " + PMC_CMD.format(c=c) for c in ("FETCH_SIZE", "WRITE_SIZE")]
@@ -412,10 +415,10 @@ def summarize_profiles(d):
     lines += ["", "Calibration: the 512 MiB copy reads and writes %d bytes; FETCH_SIZE counts %.1f KiB "
               "(factor %.4f bytes per counted byte) and WRITE_SIZE %.1f KiB (factor %.4f)." % (
                   COPY_BYTES, cf["FETCH_SIZE"], f_fac, cf["WRITE_SIZE"], w_fac), "",
-              "decode_kernel<4,64> per launch: fetch %.1f MB, write %.1f MB, total %.1f MB." % (
-                  fetch_b / 1e6, write_b / 1e6, (fetch_b + write_b) / 1e6), ""]
-    open(os.path.join(prof, "decode_kernel_%s_hbm_counters.md" % w_name), "w").write("\n".join(lines))
-    rec = {"kernel": "decode_kernel<4,64>", "workload": w_name, "kernel_source_sha256": sha,
+              "%s per launch: fetch %.1f MB, write %.1f MB, total %.1f MB." % (
+                  kname, fetch_b / 1e6, write_b / 1e6, (fetch_b + write_b) / 1e6), ""]
+    open(os.path.join(prof, "attention_%s_hbm_counters.md" % w_name), "w").write("\n".join(lines))
+    rec = {"kernel": kname, "workload": w_name, "kernel_source_sha256": sha,
            "kernel_sources": ["mla_latent_kv_41_amd/csrc/" + f for f in KERNEL_SOURCES],
            "fetch_size_kib_per_dispatch": round(dv["FETCH_SIZE"], 1),
            "write_size_kib_per_dispatch": round(dv["WRITE_SIZE"], 1),
@@ -446,7 +449,64 @@ def summarize_profiles(d):
         lines += ["", "Attention kernel source sha256 (mla_latent_kv_41_amd/csrc/decode_bf16.hip + common.hpp): `%s`"
                   % line["attention_kernel_source_sha256"], ""]
         open(os.path.join(prof, "decode_step_%s_kernel_trace.md" % wl), "w").write("\n".join(lines))
+    for c in (2, 3, 4, 5):
+        if os.path.isdir(os.path.join(d, "ctr_c%d" % c, "sq")):
+            summarize_efficiency_counters(d, c)
     print("summaries written for attention kernel source %s" % sha)
+
+
+ATTENTION_KERNELS = ("mla::decode_kernel", "mla::decode_roles_kernel")
+# Kernel-efficiency counter passes (one run each; rocprofv3 does not split counters
+# over passes): MFMA busy share, MFMA work, LDS busy share and bank conflicts; L2.
+EFF_PASSES = {"sq": "MfmaUtil LdsUtil LdsBankConflict SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE",
+              "tcc": "TCC_HIT_sum TCC_MISS_sum TCC_REQ_sum"}
+EFF_CMD = ("rocprofv3 --pmc {counters} --output-format csv -d <out>/ctr_c{c}/{p} -o {p} -- "
+           "python3 bench.py --config {c} --steps 4 --warmup 2 --no-cpu-baseline")
+
+
+def summarize_efficiency_counters(d, c):
+    """profiles/ summary of the kernel-efficiency counter passes of one workload
+    (DIR/ctr_c<N>/{sq,tcc}, logs DIR/ctr_c<N>/<pass>.log): per per-step kernel, the
+    MFMA busy share of the SIMD cycles, the bf16 MFMA work it counted, the LDS busy
+    share and bank-conflict cycles per access cycle, and the L2 hit rate."""
+    import csv
+    import glob
+    from collections import defaultdict
+    vals = defaultdict(lambda: defaultdict(list))
+    lines_of = {}
+    for p in EFF_PASSES:
+        lines_of[p] = _bench_line(os.path.join(d, "ctr_c%d" % c, p + ".log"))
+        for f in glob.glob(os.path.join(d, "ctr_c%d" % c, p, "*counter_collection.csv")):
+            for r in csv.DictReader(open(f)):
+                vals[_short_kernel_name(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    line = lines_of["sq"]
+    wl = line["config"]["workload"]
+    per_step = [k for k in vals if k.startswith(ATTENTION_KERNELS) or k.startswith(
+        ("mla::combine_kernel", "mla::qprep_kernel", "mla::splitk_gemm_kernel"))]
+    avg = lambda k, n: (sum(vals[k][n]) / len(vals[k][n])) if vals[k].get(n) else float("nan")
+    lines = ["# Kernel-efficiency counters: %s (`bench.py --config %d`)" % (wl, c), "",
+             "Commands (one pass each, from /tmp with TMPDIR=/tmp; rocprofv3 serialises the dispatches "
+             "while it counts):", ""]
+    lines += ["    " + EFF_CMD.format(counters=v, c=c, p=p) for p, v in EFF_PASSES.items()]
+    lines += ["", "Summarised with `python3 bench.py --summarize-profiles <out>`. Attention kernel source "
+              "sha256: `%s`" % line["attention_kernel_source_sha256"], "",
+              "Columns: MfmaUtil = MFMA busy cycles / (GPU busy cycles x 1024 SIMDs); MFMA GFLOP = "
+              "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 per dispatch; LdsUtil = LDS-active cycles / (GPU busy cycles x "
+              "256 CUs); LdsBankConflict = bank-conflict stall cycles per conflict-free LDS cycle; L2 hit = "
+              "TCC_HIT / (TCC_HIT + TCC_MISS); GPU busy = GRBM_GUI_ACTIVE cycles per dispatch.", "",
+              "| kernel | dispatches | MfmaUtil % | MFMA GFLOP | LdsUtil % | LdsBankConflict | L2 hit % | GPU busy cycles |",
+              "|---|---|---|---|---|---|---|---|"]
+    for k in sorted(per_step):
+        hit, miss = avg(k, "TCC_HIT_sum"), avg(k, "TCC_MISS_sum")
+        lines.append("| `%s` | %d | %.1f | %.2f | %.1f | %.4f | %.1f | %.0f |" % (
+            k, len(vals[k].get("MfmaUtil", [])), avg(k, "MfmaUtil"),
+            avg(k, "SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512 / 1e9, avg(k, "LdsUtil"), avg(k, "LdsBankConflict"),
+            100.0 * hit / (hit + miss) if hit + miss > 0 else float("nan"), avg(k, "GRBM_GUI_ACTIVE")))
+    lines += ["", "Algorithmic attention FLOPs per launch of this workload: %.2f GFLOP (the attention kernels' "
+              "MFMA work above includes the precise form's second MFMA per operand pair and the padding of "
+              "partial tiles)." % (line["roofline"]["algorithmic_flops_per_launch"] / 1e9), ""]
+    open(os.path.join(ROOT, "profiles", "efficiency_counters_%s.md" % wl), "w").write("\n".join(lines))
+    print("efficiency counters written for %s" % wl)
 
 
 APPEND_COPIES = 64  # packed down-projection copies, rotated as 64 layers would be
@@ -697,9 +757,8 @@ def main():
                 "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "mfma_TFLOPs": round(attn_tflops, 1),
                 "mfma_frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
-    rows = w.h * w.n_q
-    form = "128-row workgroups" if rows % 128 == 0 else "role-split 64-row workgroups"
-    roof.update({"kernel": "split-K attention over the latent cache (%s)" % form,
+    roof.update({"kernel": "split-K attention over the latent cache (all attention launches of a step: the fast "
+                           "form for sequences of 4096 tokens or more, the precise form below)",
                  "algorithmic_bytes_per_launch": cache_bytes, "algorithmic_flops_per_launch": attn_flops})
     out = {
         "metric": "MLA decode TFLOP/s + latent-cache GB/s (% roofline), h=128 B=32 ctx=4096",

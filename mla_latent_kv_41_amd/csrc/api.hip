@@ -74,7 +74,8 @@ struct Plan {
   int fast_form;     // kForm128 (rows a multiple of 128) or kFormRoles
   int fast_groups;   // head groups (workgroups) per pair in the fast form
   int prec_groups;   // ... in the precise form (64-row workgroups)
-  int chunk;         // tokens per range, a multiple of kTile
+  int chunk;         // tokens per range of the fast form's sequences, a multiple of kTile
+  int chunk_precise; // ... of the precise form's sequences
   int64_t cap;       // pairs the workspace holds: a bound on Σ_b ceil(kv_b / chunk)
   int64_t fast_pairs, prec_pairs;  // bounds on the pairs of each list (0: not launched)
   int comb_rows;     // combine: query rows per workgroup (<= 32)
@@ -135,12 +136,30 @@ Plan plan_bf16(const Resolved& r, const mla_decode_args* a) {
   chunk = std::max(chunk, ceil_div(L, kMaxSplitsPerSeq));
   chunk = ceil_div(chunk, kTile) * kTile;
   p.chunk = static_cast<int>(std::min<int64_t>(chunk, ceil_div(L, kTile) * kTile));
+  p.chunk_precise = p.chunk;
+  if (a->kv_lens_host && a->num_splits == 0) {
+    // when both forms run, the precise launch follows the fast one on its own: size
+    // its ranges so its sequences' units fill the chip once (at least kMinRaggedChunk
+    // tokens), rather than by the fast form's ranges
+    int64_t prec_units = 0;
+    bool any_fast = false;
+    for (int b = 0; b < a->batch; ++b) {
+      const int64_t kv = std::min<int64_t>(a->kv_lens_host[b], L);
+      if (kv < kPreciseBelow) prec_units += kv * p.prec_groups;
+      else any_fast = true;
+    }
+    if (any_fast && prec_units > 0) {
+      const int64_t c = std::max<int64_t>(kMinRaggedChunk, ceil_div(prec_units, target));
+      p.chunk_precise = static_cast<int>(std::min<int64_t>(ceil_div(c, kTile) * kTile, ceil_div(L, kTile) * kTile));
+    }
+  }
   if (a->kv_lens_host) {
     for (int b = 0; b < a->batch; ++b) {
       const int64_t kv = std::min<int64_t>(a->kv_lens_host[b], L);
-      const int64_t ns = kv >= a->n_q ? ceil_div(kv, p.chunk) : 0;
+      const bool prec = kv < kPreciseBelow;
+      const int64_t ns = kv >= a->n_q ? ceil_div(kv, prec ? p.chunk_precise : p.chunk) : 0;
       p.cap += ns;
-      (kv < kPreciseBelow ? p.prec_pairs : p.fast_pairs) += ns;
+      (prec ? p.prec_pairs : p.fast_pairs) += ns;
     }
   } else {
     // any length up to max_kv_len: both lists may fill
@@ -308,7 +327,8 @@ mla_status decode_impl(const mla_dims* dims, const CacheRef& cache, const mla_de
   q.plan.batch = a->batch;
   q.plan.n_q = a->n_q;
   q.plan.max_kv_len = a->max_kv_len;
-  q.plan.chunk = p.chunk;
+  q.plan.chunk_fast = p.chunk;
+  q.plan.chunk_precise = p.chunk_precise;
   q.plan.precise_below = kPreciseBelow;
   q.plan.cap = static_cast<int32_t>(p.cap);
   q.plan.counts = counts;
@@ -353,6 +373,7 @@ mla_status decode_impl(const mla_dims* dims, const CacheRef& cache, const mla_de
   if (prec_units > 0) {
     d.list = prec_list;
     d.count = counts + 1;
+    d.chunk = p.chunk_precise;
     d.form = kFormPrecise;
     d.units = static_cast<int32_t>(prec_units);
     if (launch_decode_bf16(d, stream, two ? nullptr : a->ev_attn_begin, a->ev_attn_end) != hipSuccess)

@@ -33,14 +33,14 @@ struct WorkItem {
 };
 
 // Split plan built on the device (by the query preparation's first workgroup) from
-// kv_lens: sequence b holds ns_b = ceil(kv_b / chunk) ranges (none if kv_b < n_q);
-// their partials take indices seq_off[b] .. seq_off[b] + ns_b - 1, compactly. A
-// sequence with fewer than precise_below tokens goes to the precise list, else to
-// the fast list. Pairs past `cap` are dropped (only possible when the host lengths
-// the plan was sized from disagree with kv_lens).
+// kv_lens: a sequence with fewer than precise_below tokens goes to the precise list
+// and holds ns_b = ceil(kv_b / chunk_precise) ranges, else to the fast list with
+// ceil(kv_b / chunk_fast) ranges (none if kv_b < n_q); its partials take indices
+// seq_off[b] .. seq_off[b] + ns_b - 1, compactly. Pairs past `cap` are dropped
+// (only possible when the host lengths the plan was sized from disagree with kv_lens).
 struct PlanArgs {
   const int32_t* kv_lens;
-  int32_t batch, n_q, max_kv_len, chunk, precise_below, cap;
+  int32_t batch, n_q, max_kv_len, chunk_fast, chunk_precise, precise_below, cap;
   int32_t* counts;    // [0] pairs in the fast list, [1] in the precise list
   int32_t* seq_off;   // [batch + 1]
   WorkItem* fast;     // [cap]

@@ -73,7 +73,8 @@ __device__ void build_plan(const PlanArgs& p, int l) {
   auto splits = [&](int b, int* kv_out) __attribute__((always_inline)) {
     const int kv = min(max(p.kv_lens[b], 0), p.max_kv_len);
     *kv_out = kv;
-    return kv >= p.n_q ? (kv + p.chunk - 1) / p.chunk : 0;
+    const int chunk = kv < p.precise_below ? p.chunk_precise : p.chunk_fast;
+    return kv >= p.n_q ? (kv + chunk - 1) / chunk : 0;
   };
   int tot = 0, nf = 0, np = 0;
   for (int b = b0; b < b1; ++b) {
