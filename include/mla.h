@@ -185,6 +185,43 @@ mla_status mla_decode_noalloc(const mla_dims* dims, const void* cache, const mla
                               const mla_decode_args* args, hipStream_t stream);
 
 /*
+ * The non-absorbed form, for comparison with the absorbed decode (tutorial §3.2:
+ * the training-time forward up-projects the cached latent into per-head keys and
+ * values, k = c_KV · W_UK and v = c_KV · W_UV, and runs standard attention; §3.3
+ * compares the two forms at decode). MLA_BF16 only, d_qk_nope = d_v = 128.
+ *
+ * mla_expand_kv writes, for every cached token t < kv_lens[b] of every sequence,
+ *   k_out[b][t][i][e] = Σ_c c_t[c] · W_UK[c][i*128 + e]
+ *   v_out[b][t][i][e] = Σ_c c_t[c] · W_UV[c][i*128 + e]
+ * in fp32 (bf16 products on the matrix cores, fp32 accumulation), with k_out and
+ * v_out device [batch][max_kv_len][h][128] fp32 (rows past kv_lens[b] untouched).
+ *   cache, layout  the latent cache, as for mla_append_latent
+ *   kv_lens        device [batch]; values above max_kv_len are clamped to it
+ *   w_uk, w_uv     device [d_c][h*128] bf16, the formula layout (not packed)
+ *   workspace      device scratch for the weights in matrix-core order, or NULL to
+ *                  query its size (2 * d_c * h * 128 * 2 bytes, rounded up)
+ */
+mla_status mla_expand_kv(const mla_dims* dims, const void* cache, const mla_cache_layout* layout, int32_t batch,
+                         const int32_t* kv_lens, int32_t max_kv_len, const void* w_uk, const void* w_uv,
+                         float* k_out, float* v_out, void* workspace, size_t* workspace_bytes,
+                         hipStream_t stream);
+
+/*
+ * Standard attention over explicit keys and values (the non-absorbed decode): for
+ * query j of sequence b and head i, the scores
+ *   scale · ( q_nope · k[b][t][i] + RoPE(q_R, p_j) · k_R,t ),  t <= p_j = kv_len - n_q + j,
+ * with k_R the rotated key stored in the latent cache rows (one per token, shared by
+ * the heads), a max-subtracted softmax and out = Σ_t p_t v[b][t][i]; the gate as in
+ * mla_decode. fp32 arithmetic throughout. k, v are [batch][args->max_kv_len][h][128]
+ * fp32, as mla_expand_kv writes them for the same max_kv_len. args as for mla_decode
+ * (packed_w is not used; n_q <= 4); the workspace holds the token ranges' partial
+ * results (size query with workspace == NULL). Timing events, when given, are
+ * recorded on `stream` around the attention kernel.
+ */
+mla_status mla_decode_explicit(const mla_dims* dims, const float* k, const float* v, const void* cache,
+                               const mla_cache_layout* layout, const mla_decode_args* args, hipStream_t stream);
+
+/*
  * Fused latent append from the hidden state: the cache row of each new token,
  *   [ gain ⊙ c / sqrt(mean(c²) + eps)  ‖  RoPE(h · W_KR, pos) ],  c = h · W_DKV,
  * computed and stored in one call (tutorial §2.2: c_KV = h · W_DKV with W_DKV of

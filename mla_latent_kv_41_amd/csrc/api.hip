@@ -516,6 +516,124 @@ mla_status mla_decode_noalloc(const mla_dims* dims, const void* cache, const mla
   return decode_impl(dims, c, &la, stream);
 }
 
+mla_status mla_expand_kv(const mla_dims* dims, const void* cache, const mla_cache_layout* layout, int32_t batch,
+                         const int32_t* kv_lens, int32_t max_kv_len, const void* w_uk, const void* w_uv,
+                         float* k_out, float* v_out, void* workspace, size_t* workspace_bytes,
+                         hipStream_t stream) {
+  Resolved r;
+  mla_status st = resolve(dims, &r);
+  if (st != MLA_OK) return st;
+  if (!layout || !workspace_bytes) return MLA_E_NULL;
+  if (r.dtype != MLA_BF16) return MLA_E_UNSUPPORTED;
+  if (batch <= 0 || max_kv_len <= 0) return MLA_E_SHAPE;
+  if (layout->block_table) {
+    if (layout->block_size <= 0 || layout->max_blocks <= 0 || layout->n_blocks <= 0) return MLA_E_SHAPE;
+    if (static_cast<int64_t>(layout->max_blocks) * layout->block_size < max_kv_len) return MLA_E_SHAPE;
+  } else if (layout->t_max < max_kv_len) {
+    return MLA_E_SHAPE;
+  }
+  if (static_cast<int64_t>(batch) * ceil_div(max_kv_len, 128) > INT32_MAX || r.h > 65535) return MLA_E_UNSUPPORTED;
+  const size_t need = align_up(2 * static_cast<size_t>(r.h) * 128 * r.d_c * 2);
+  if (!workspace) {
+    *workspace_bytes = need;
+    return MLA_OK;
+  }
+  if (*workspace_bytes < need) return MLA_E_WORKSPACE;
+  if (!cache || !kv_lens || !w_uk || !w_uv || !k_out || !v_out) return MLA_E_NULL;
+  ExpandArgs e{};
+  e.cache = CacheRef{cache, layout->block_table, layout->t_max, layout->block_size, layout->max_blocks,
+                     layout->n_blocks};
+  e.kv_lens = kv_lens;
+  e.w_uk = static_cast<const uint16_t*>(w_uk);
+  e.w_uv = static_cast<const uint16_t*>(w_uv);
+  e.packed = static_cast<const uint16_t*>(workspace);
+  e.k_out = k_out;
+  e.v_out = v_out;
+  e.batch = batch;
+  e.max_kv_len = max_kv_len;
+  e.h = r.h;
+  e.d_c = r.d_c;
+  e.d_r = r.d_r;
+  return launch_expand(e, stream) == hipSuccess ? MLA_OK : MLA_E_HIP;
+}
+
+mla_status mla_decode_explicit(const mla_dims* dims, const float* k, const float* v, const void* cache,
+                               const mla_cache_layout* layout, const mla_decode_args* a, hipStream_t stream) {
+  Resolved r;
+  mla_status st = resolve(dims, &r);
+  if (st != MLA_OK) return st;
+  if (!a || !layout || !a->workspace_bytes) return MLA_E_NULL;
+  if (r.dtype != MLA_BF16) return MLA_E_UNSUPPORTED;
+  if (a->batch <= 0 || a->n_q <= 0 || a->max_kv_len < a->n_q || a->num_splits < 0) return MLA_E_SHAPE;
+  if (a->n_q > 4) return MLA_E_UNSUPPORTED;
+  if ((a->gate_x == nullptr) != (a->w_gate == nullptr)) return MLA_E_NULL;
+  if ((a->ev_attn_begin == nullptr) != (a->ev_attn_end == nullptr)) return MLA_E_NULL;
+  if (a->gate_x && (a->d_model <= 0 || a->d_model % (kGateSplit * 16) != 0)) return MLA_E_UNSUPPORTED;
+  if (a->kv_lens_host)
+    for (int b = 0; b < a->batch; ++b)
+      if (a->kv_lens_host[b] < a->n_q || a->kv_lens_host[b] > a->max_kv_len) return MLA_E_SHAPE;
+  if (layout->block_table) {
+    if (layout->block_size <= 0 || layout->max_blocks <= 0 || layout->n_blocks <= 0) return MLA_E_SHAPE;
+    if (static_cast<int64_t>(layout->max_blocks) * layout->block_size < a->max_kv_len) return MLA_E_SHAPE;
+  } else if (layout->t_max < a->max_kv_len) {
+    return MLA_E_SHAPE;
+  }
+  // token ranges: enough (sequence, head, range) workgroups to fill the chip a few times
+  const int64_t L = a->max_kv_len, M = static_cast<int64_t>(a->batch) * a->n_q;
+  int64_t splits = a->num_splits > 0 ? a->num_splits
+                                     : std::min(ceil_div(2048, static_cast<int64_t>(a->batch) * r.h), ceil_div(L, 256));
+  splits = std::max<int64_t>(1, std::min(splits, L));
+  const int64_t chunk = ceil_div(ceil_div(L, splits), 8) * 8;
+  splits = ceil_div(L, chunk);
+  if (static_cast<int64_t>(a->batch) * splits * r.h > INT32_MAX) return MLA_E_UNSUPPORTED;
+  size_t off = 0;
+  const size_t part_off = off;
+  off = align_up(off + static_cast<size_t>(a->batch) * splits * a->n_q * r.h * 130 * 4);
+  const size_t gate_off = off;
+  if (a->gate_x) off = align_up(off + static_cast<size_t>(kGateSplit) * M * r.h * 128 * 4);
+  if (!a->workspace) {
+    *a->workspace_bytes = off;
+    return MLA_OK;
+  }
+  if (*a->workspace_bytes < off) return MLA_E_WORKSPACE;
+  if (!k || !v || !cache || !a->kv_lens || !a->q_nope || !a->out) return MLA_E_NULL;
+  if (r.d_r > 0 && !a->q_rope) return MLA_E_NULL;
+  char* wsb = static_cast<char*>(a->workspace);
+  if (a->gate_x) {
+    GemmArgs g{};
+    g.x = static_cast<const uint16_t*>(a->gate_x);
+    g.w = static_cast<const uint16_t*>(a->w_gate);
+    g.g = reinterpret_cast<float*>(wsb + gate_off);
+    g.M = static_cast<int32_t>(M);
+    g.K = a->d_model;
+    g.N = r.h * 128;
+    g.ksplit = kGateSplit;
+    if (launch_splitk_gemm_bf16(g, stream) != hipSuccess) return MLA_E_HIP;
+  }
+  ExplicitArgs e{};
+  e.cache = CacheRef{cache, layout->block_table, layout->t_max, layout->block_size, layout->max_blocks,
+                     layout->n_blocks};
+  e.kv_lens = a->kv_lens;
+  e.k = k;
+  e.v = v;
+  e.q_nope = static_cast<const uint16_t*>(a->q_nope);
+  e.q_rope = static_cast<const uint16_t*>(a->q_rope);
+  e.gate = a->gate_x ? reinterpret_cast<const float*>(wsb + gate_off) : nullptr;
+  e.part = reinterpret_cast<float*>(wsb + part_off);
+  e.out = a->out;
+  e.lse = a->lse;
+  e.batch = a->batch;
+  e.n_q = a->n_q;
+  e.h = r.h;
+  e.d_r = r.d_r;
+  e.max_kv_len = a->max_kv_len;
+  e.n_splits = static_cast<int32_t>(splits);
+  e.chunk = static_cast<int32_t>(chunk);
+  e.qscale = r.scale * 1.4426950408889634f;
+  for (int q = 0; q < r.d_r / 2 && q < 32; ++q) e.inv_freq[q] = pow(r.rope_base, -2.0 * q / r.d_r);
+  return launch_explicit_decode(e, a->ev_attn_begin, a->ev_attn_end, stream) == hipSuccess ? MLA_OK : MLA_E_HIP;
+}
+
 mla_status mla_pack_down_weights(const mla_dims* dims, int32_t d_model, const void* w_dkv, const void* w_kr,
                                  void* packed, size_t* packed_bytes, hipStream_t stream) {
   Resolved r;

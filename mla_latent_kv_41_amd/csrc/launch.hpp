@@ -105,6 +105,36 @@ struct GemmArgs {
 };
 hipError_t launch_splitk_gemm_bf16(const GemmArgs& a, hipStream_t s);
 
+// ---------------------------------------------------------------- non-absorbed form
+struct ExpandArgs {
+  CacheRef cache;             // the latent cache (bf16)
+  const int32_t* kv_lens;     // [batch]
+  const uint16_t* w_uk;       // [d_c][h*128] formula layout
+  const uint16_t* w_uv;       // [d_c][h*128]
+  const uint16_t* packed;     // workspace: both matrices in B-fragment order (written first)
+  float* k_out;               // [batch][max_kv_len][h][128]
+  float* v_out;               // [batch][max_kv_len][h][128]
+  int32_t batch, max_kv_len, h, d_c, d_r;
+};
+hipError_t launch_expand(const ExpandArgs& a, hipStream_t s);
+
+struct ExplicitArgs {
+  CacheRef cache;             // the latent cache, for the rotated keys k_R
+  const int32_t* kv_lens;
+  const float* k;             // [batch][max_kv_len][h][128]
+  const float* v;             // [batch][max_kv_len][h][128]
+  const uint16_t* q_nope;     // [batch][n_q][h][128]
+  const uint16_t* q_rope;     // [batch][n_q][h][d_r] or nullptr
+  const float* gate;          // [16][M][h*128] gate logit splits, or nullptr
+  float* part;                // [batch][n_splits][n_q][h][130] (O, m, l) per token range
+  float* out;                 // [M][h*128]
+  float* lse;                 // [M][h] or nullptr
+  int32_t batch, n_q, h, d_r, max_kv_len, n_splits, chunk;
+  float qscale;               // scale * log2(e)
+  double inv_freq[32];        // rope_base^(-2k/d_r)
+};
+hipError_t launch_explicit_decode(const ExplicitArgs& a, hipEvent_t ev0, hipEvent_t ev1, hipStream_t s);
+
 // ---------------------------------------------------------------- fused append
 // Cache row [gain ⊙ RMSNorm(h · W_DKV) ‖ RoPE(h · W_KR, pos)] of each new token.
 constexpr int kMaxRopePairs = 128;  // d_r <= 256

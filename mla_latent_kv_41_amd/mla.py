@@ -18,7 +18,8 @@ MLA_OK, MLA_E_NULL, MLA_E_SHAPE, MLA_E_DTYPE, MLA_E_UNSUPPORTED, MLA_E_WORKSPACE
 MLA_F32, MLA_BF16 = 0, 1
 
 EXPORTS = ("mla_absorb_weights", "mla_append_latent", "mla_decode", "mla_decode_paged",
-           "mla_decode_noalloc", "mla_pack_down_weights", "mla_project_append", "mla_status_string")
+           "mla_decode_noalloc", "mla_expand_kv", "mla_decode_explicit", "mla_pack_down_weights",
+           "mla_project_append", "mla_status_string")
 
 
 class MLAError(RuntimeError):
@@ -87,6 +88,12 @@ def lib():
         L.mla_decode_noalloc.restype = st
         L.mla_decode_noalloc.argtypes = [ctypes.POINTER(mla_dims), vp, ctypes.POINTER(mla_cache_layout),
                                          ctypes.POINTER(mla_decode_args), vp]
+        L.mla_expand_kv.restype = st
+        L.mla_expand_kv.argtypes = [ctypes.POINTER(mla_dims), vp, ctypes.POINTER(mla_cache_layout), ctypes.c_int32,
+                                    vp, ctypes.c_int32, vp, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_size_t), vp]
+        L.mla_decode_explicit.restype = st
+        L.mla_decode_explicit.argtypes = [ctypes.POINTER(mla_dims), vp, vp, vp, ctypes.POINTER(mla_cache_layout),
+                                          ctypes.POINTER(mla_decode_args), vp]
         L.mla_pack_down_weights.restype = st
         L.mla_pack_down_weights.argtypes = [ctypes.POINTER(mla_dims), ctypes.c_int32, vp, vp, vp,
                                             ctypes.POINTER(ctypes.c_size_t), vp]
@@ -329,6 +336,49 @@ def mla_decode_noalloc(d: mla_dims, cache, *, kv_lens, max_kv_len: int, q_nope, 
                             workspace_bytes=0, num_splits=num_splits, events=events)
     return _check(lib().mla_decode_noalloc(ctypes.byref(d), _ptr(cache), ctypes.byref(layout), ctypes.byref(a),
                                            _stream(stream)), "mla_decode_noalloc")
+
+
+def mla_expand_kv(d: mla_dims, cache, *, kv_lens, max_kv_len: int, w_uk, w_uv, k_out, v_out, batch: int,
+                  t_max: int = 0, block_table=None, block_size: int = 0, max_blocks: int = 0, n_blocks: int = 0,
+                  workspace=None, stream=None) -> int:
+    """Explicit per-head K and V (fp32) of every cached token: the non-absorbed form."""
+    layout = mla_cache_layout(_ptr(block_table), t_max, block_size, max_blocks, n_blocks)
+
+    def query():
+        n = ctypes.c_size_t(0)
+        _check(lib().mla_expand_kv(ctypes.byref(d), None, ctypes.byref(layout), batch, None, max_kv_len, None,
+                                   None, None, None, None, ctypes.byref(n), None), "mla_expand_kv")
+        return n.value
+
+    ws = _workspace_for(query, workspace, w_uk.device)
+    n = ctypes.c_size_t(ws.numel() * ws.element_size())
+    return _check(lib().mla_expand_kv(ctypes.byref(d), _ptr(cache), ctypes.byref(layout), batch, _ptr(kv_lens),
+                                      max_kv_len, _ptr(w_uk), _ptr(w_uv), _ptr(k_out), _ptr(v_out), _ptr(ws),
+                                      ctypes.byref(n), _stream(stream)), "mla_expand_kv")
+
+
+def mla_decode_explicit(d: mla_dims, k, v, cache, *, kv_lens, max_kv_len: int, q_nope, q_rope, out,
+                        t_max: int = 0, block_table=None, block_size: int = 0, max_blocks: int = 0,
+                        n_blocks: int = 0, kv_lens_host: Optional[Sequence[int]] = None, gate_x=None,
+                        w_gate=None, lse=None, workspace=None, num_splits: int = 0, events=None,
+                        stream=None) -> int:
+    """Standard attention over explicit per-head K and V (the non-absorbed decode)."""
+    B, n_q = q_nope.shape[0], q_nope.shape[1]
+    layout = mla_cache_layout(_ptr(block_table), t_max, block_size, max_blocks, n_blocks)
+    common = dict(batch=B, n_q=n_q, kv_lens=kv_lens, kv_lens_host=kv_lens_host, max_kv_len=max_kv_len,
+                  q_nope=q_nope, q_rope=q_rope, packed_w=None, gate_x=gate_x, w_gate=w_gate, out=out, lse=lse,
+                  num_splits=num_splits, events=events)
+
+    def query():
+        a, n, _h = _decode_args(workspace=None, workspace_bytes=0, **common)
+        _check(lib().mla_decode_explicit(ctypes.byref(d), None, None, None, ctypes.byref(layout), ctypes.byref(a),
+                                         None), "mla_decode_explicit")
+        return n.value
+
+    ws = _workspace_for(query, workspace, q_nope.device)
+    a, n, _h = _decode_args(workspace=ws, workspace_bytes=ws.numel() * ws.element_size(), **common)
+    return _check(lib().mla_decode_explicit(ctypes.byref(d), _ptr(k), _ptr(v), _ptr(cache), ctypes.byref(layout),
+                                            ctypes.byref(a), _stream(stream)), "mla_decode_explicit")
 
 
 def decode_workspace_bytes(d: mla_dims, *, batch: int, n_q: int, max_kv_len: int,

@@ -176,6 +176,29 @@ def unabsorbed_flops(h, d_c, d_n, d_v, d_r, kv_lens, n_q, d_model=0) -> float:
     return proj + attn + gate
 
 
+def explicit_kv(*, c_kv, w_uk, w_uv, kv_lens, h: int, d_n: int, d_v: int):
+    """The explicit per-head keys and values of every cached token, the form the
+    non-absorbed decode attends over (MLA tutorial page §3.2: k = c_KV · W_UK and
+    v = c_KV · W_UV; §2.2 for the head split of W_UK and W_UV): fp64
+    ``K [B, T, h, d_n]`` and ``V [B, T, h, d_v]`` from ``c_kv [B, T, d_c]`` and the
+    formula-layout ``w_uk [d_c, h*d_n]``, ``w_uv [d_c, h*d_v]`` (one dtype: float64,
+    float32 or bf16 bits). Slots past ``kv_lens[b]`` are NaN."""
+    def f64(a):
+        a = np.asarray(a)
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64) if a.dtype == np.uint16 \
+            else a.astype(np.float64)
+    c = f64(c_kv)
+    uk, uv = f64(w_uk), f64(w_uv)
+    B, T, _ = c.shape
+    K = np.full((B, T, h, d_n), np.nan)
+    V = np.full((B, T, h, d_v), np.nan)
+    for b in range(B):
+        n = int(kv_lens[b])
+        K[b, :n] = (c[b, :n] @ uk).reshape(n, h, d_n)
+        V[b, :n] = (c[b, :n] @ uv).reshape(n, h, d_v)
+    return K, V
+
+
 def round_bf16_array(x) -> np.ndarray:
     """Nearest-even bf16 value of every element (fp64 in, fp64 out)."""
     x = np.ascontiguousarray(x, np.float64)

@@ -507,3 +507,36 @@ def test_unabsorbed_flops_counts_what_the_definition_executes():
     for h, d_c, d_n, d_v, d_r, kv, n_q, dm in cases:
         assert oracle.unabsorbed_flops(h, d_c, d_n, d_v, d_r, kv, n_q, d_model=dm) == \
             _count_explicit_ops(h, d_c, d_n, d_v, d_r, kv, n_q, dm)
+
+
+def test_explicit_kv_attended_by_torch_equals_the_oracle():
+    """oracle.explicit_kv (numpy products) gives the keys and values whose standard
+    attention, in torch's fp64 scaled_dot_product_attention with the rotated keys
+    the cache stores, equals the oracle's own explicit form (C loops) to 1e-12:
+    multi-query causal, ragged lengths, with the RoPE key."""
+    w = synth.make_workload(4, batch=3, ctx_range=(20, 90))
+    t = synth.draw(w)
+    K, V = oracle.explicit_kv(c_kv=t["c_kv"], w_uk=t["w_uk"], w_uv=t["w_uv"], kv_lens=w.kv_lens,
+                              h=w.h, d_n=w.d_n, d_v=w.d_v)
+    kr = oracle.cache_keys(d_r=w.d_r, k_r=t["k_r"], kv_lens=w.kv_lens, store_bf16=False)
+    qn, qr_raw = as_f64(t["q_nope"]), as_f64(t["q_r"])
+    out = np.zeros((w.batch, w.n_q, w.h * w.d_v))
+    for b in range(w.batch):
+        T = int(w.kv_lens[b])
+        Kb = np.concatenate([K[b, :T].transpose(1, 0, 2), np.broadcast_to(kr[b, :T][None], (w.h, T, w.d_r))], -1)
+        q = np.concatenate([qn[b].transpose(1, 0, 2),
+                            np.stack([rope_complex(qr_raw[b, j], T - w.n_q + j) for j in range(w.n_q)], 1)], -1)
+        mask = np.arange(T)[None, :] <= (T - w.n_q + np.arange(w.n_q))[:, None]
+        o = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(np.ascontiguousarray(q)), torch.from_numpy(np.ascontiguousarray(Kb)),
+            torch.from_numpy(np.ascontiguousarray(V[b, :T].transpose(1, 0, 2))),
+            attn_mask=torch.from_numpy(mask)).numpy()
+        out[b] = o.transpose(1, 0, 2).reshape(w.n_q, -1)
+    assert rel_err(out, run_oracle(w, t, store_bf16=False)) < 1e-12
+    # identity up-projections: each head's key and value are its slice of the latent
+    c = np.random.default_rng(3).normal(size=(1, 5, 8))
+    eye = np.eye(8)
+    K1, V1 = oracle.explicit_kv(c_kv=c, w_uk=eye, w_uv=eye, kv_lens=[4], h=2, d_n=4, d_v=4)
+    np.testing.assert_array_equal(K1[0, :4], c[0, :4].reshape(4, 2, 4))
+    np.testing.assert_array_equal(V1[0, :4], c[0, :4].reshape(4, 2, 4))
+    assert np.isnan(K1[0, 4]).all()
