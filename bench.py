@@ -758,6 +758,103 @@ def bench_explicit(args):
         "results": results}), flush=True)
 
 
+def bench_folded(args):
+    """Weight-level absorption (MLA tutorial page §2.2: W_UK folded into the query's
+    up-projection W_UQ, W_UV into the output projection W_O) against the runtime
+    absorption the library does, on the DeepSeek-shaped layer from the query latent
+    c_Q (d_q = 512, the tutorial's §4.2 choice) to the layer output (d_model = 4096):
+
+      runtime: q_nope = c_Q · W_UQ;  mla_decode (W_UK and W_UV applied per step);
+               y = out · W_O         weights per step 16.8 + 33.6 + 134.2 MB
+      folded:  q_abs = c_Q · W_UQK;  mla_decode_latent;  y = o_lat · W_UVO
+               weights per step 67.1 + 536.9 MB
+
+    The projections are plain bf16 products (torch, i.e. hipBLASLt); three copies of
+    every weight set rotate as three layers would, so none stays in the 256 MB
+    Infinity Cache. Reports each form's step time and its parts."""
+    import numpy as np
+    import torch
+    from mla_latent_kv_41_amd import mla, synth
+    from mla_latent_kv_41_amd.harness import GpuStep
+
+    w = synth.make_workload(2)
+    t = synth.draw(w)
+    d_q, d_model = 512, 4096
+    steps = [GpuStep(w, t, poison=False) for _ in range(COPIES)]
+    for st in steps[1:]:
+        st.q_rope, st.out, st.lse = steps[0].q_rope, steps[0].out, steps[0].lse
+    g = torch.Generator(device="cuda").manual_seed(4103)
+    bf = torch.bfloat16
+    M, H = w.batch * w.n_q, w.h
+    c_q = torch.randn(M, d_q, device="cuda", generator=g).to(bf)
+    rt = [(torch.randn(d_q, H * 128, device="cuda", generator=g).div_(d_q ** 0.5).to(bf),
+           torch.randn(H * 128, d_model, device="cuda", generator=g).div_((H * 128) ** 0.5).to(bf))
+          for _ in range(COPIES)]
+    fd = [(torch.randn(d_q, H * 512, device="cuda", generator=g).div_(d_q ** 0.5).to(bf),
+           torch.randn(H * 512, d_model, device="cuda", generator=g).div_((H * 512) ** 0.5).to(bf))
+          for _ in range(COPIES)]
+    o_lat = torch.empty(M, H, 512, dtype=torch.float32, device="cuda")
+    ws_lat = [None]
+
+    def runtime(k):
+        st = steps[k % COPIES]
+        w_uq, w_o = rt[k % COPIES]
+        st.q_nope = (c_q @ w_uq).view(w.batch, w.n_q, H, 128)
+        st.decode()
+        return st.out.view(M, H * 128).to(bf) @ w_o
+
+    def folded(k):
+        st = steps[k % COPIES]
+        w_uqk, w_uvo = fd[k % COPIES]
+        q_abs = (c_q @ w_uqk).float().view(w.batch, w.n_q, H, 512)
+        mla.mla_decode_latent(st.dims, st.cache, kv_lens=st.kv_lens, max_kv_len=w.kv_max, q_abs=q_abs,
+                              q_rope=st.q_rope, o_lat=o_lat, t_max=st.t_max, kv_lens_host=st.kv_lens_host,
+                              workspace=ws_lat[0])
+        return o_lat.view(M, H * 512).to(bf) @ w_uvo
+
+    def timed(fn, n):
+        t0 = time.perf_counter()
+        k = 0
+        while time.perf_counter() - t0 < SETTLE_S:
+            fn(k)
+            k += 1
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for k in range(n):
+            fn(k)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    n = max(args.steps, 20)
+    ms_rt = timed(runtime, n)
+    ms_fd = timed(folded, n)
+    ms_rt_q = timed(lambda k: c_q @ rt[k % COPIES][0], n)
+    ms_rt_o = timed(lambda k: steps[0].out.view(M, H * 128).to(bf) @ rt[k % COPIES][1], n)
+    ms_fd_q = timed(lambda k: (c_q @ fd[k % COPIES][0]).float(), n)
+    ms_fd_o = timed(lambda k: o_lat.view(M, H * 512).to(bf) @ fd[k % COPIES][1], n)
+    rt_bytes = 2.0 * (d_q * H * 128 + 2 * 512 * H * 128 + H * 128 * d_model)
+    fd_bytes = 2.0 * (d_q * H * 512 + H * 512 * d_model)
+    flops_abs, cache_bytes, _ = algorithmic(w)
+    rt_flops = flops_abs + 2.0 * M * (d_q * H * 128 + H * 128 * d_model)
+    fd_flops = flops_abs - 2.0 * H * M * 128 * 512 * 2 + 2.0 * M * (d_q * H * 512 + H * 512 * d_model)
+    out = {
+        "metric": "weight-level vs runtime absorption: MLA layer step (c_Q -> y) latency, DeepSeek-shaped",
+        "value": round(ms_fd / ms_rt, 3), "unit": "folded / runtime step time", "n_gpus": 1, "steps": n,
+        "higher_is_better": False, "dtype": "bf16", "data": "synthetic (seeded)",
+        "config": {"workload": "weight_folding_deepseek_b32_ctx4096", "d_q": d_q, "d_model": d_model,
+                   "weight_copies_rotated": COPIES},
+        "runtime_step_ms": round(ms_rt, 5), "folded_step_ms": round(ms_fd, 5),
+        "runtime_parts_ms": {"c_Q·W_UQ": round(ms_rt_q, 5), "out·W_O": round(ms_rt_o, 5)},
+        "folded_parts_ms": {"c_Q·W_UQK": round(ms_fd_q, 5), "o_lat·W_UVO": round(ms_fd_o, 5)},
+        "weight_bytes_per_step": {"runtime": rt_bytes, "folded": fd_bytes},
+        "flops_per_step": {"runtime": rt_flops, "folded": fd_flops},
+        "latent_cache_bytes": cache_bytes,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -769,10 +866,11 @@ def main():
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5],
                     help="workload: 2 DeepSeek-shaped (default, the headline), 3 paged long "
                          "context, 4 ragged with two queries, 5 gated h=64 without RoPE")
-    ap.add_argument("--workload", default="decode", choices=["decode", "append", "explicit"],
+    ap.add_argument("--workload", default="decode", choices=["decode", "append", "explicit", "folded"],
                     help="decode: the decode step (default); append: the fused latent append "
                          "from the hidden state (mla_project_append); explicit: the absorbed step "
-                         "against the non-absorbed form (mla_expand_kv + mla_decode_explicit)")
+                         "against the non-absorbed form (mla_expand_kv + mla_decode_explicit); "
+                         "folded: weight-level absorption (mla_decode_latent) against the runtime form")
     ap.add_argument("--k-splits", type=int, default=0,
                     help="append workload: force the d_model splits of the product (0: library)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
@@ -791,6 +889,9 @@ def main():
         return
     if args.workload == "explicit":
         bench_explicit(args)
+        return
+    if args.workload == "folded":
+        bench_folded(args)
         return
 
     import numpy as np

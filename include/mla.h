@@ -165,6 +165,27 @@ mla_status mla_decode_paged(const mla_dims* dims, const void* pool, const int32_
                             const mla_decode_args* args, hipStream_t stream);
 
 /*
+ * Decode with the absorption folded into the weights (tutorial §2.2 and §5.1: W_UK
+ * can be absorbed into the query's up-projection W_UQ, and W_UV into the output
+ * projection W_O, so neither is applied at run time). The caller forms the absorbed
+ * query itself, q_abs = c_Q · (W_UQ_i · W_UK_iᵀ), and applies the folded output
+ * weights (W_UV_i · W_O_i) to the result; this call runs the attention between:
+ *   args->q_nope  device [B][n_q][h][d_c] fp32: the absorbed query q_abs (not q_nope),
+ *                 rounded once by the call, with the score scale, to the matrix cores'
+ *                 bf16 (a hi + lo pair for the sequences the precise form takes)
+ *   args->q_rope  device [B][n_q][h][d_rope] unrotated, as for mla_decode
+ *   args->out     device [B][n_q][h][d_c] fp32: the merged latent output
+ *                 o_lat = Σ_t p_t c_t of each (query, head), not yet up-projected
+ * The scores are scale · (q_abs · c_t + RoPE(q_R) · k_R,t) with the same attention
+ * kernels and plan as mla_decode; args->packed_w is not used; args->lse as there.
+ * `layout` selects the cache form (contiguous when block_table is NULL). The gate
+ * acts on the heads' outputs, which this form never forms: a gated call returns
+ * MLA_E_UNSUPPORTED. MLA_BF16 only.
+ */
+mla_status mla_decode_latent(const mla_dims* dims, const void* cache, const mla_cache_layout* layout,
+                             const mla_decode_args* args, hipStream_t stream);
+
+/*
  * Allocation-free decode, for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same computation and kernels as mla_decode / mla_decode_paged, with the

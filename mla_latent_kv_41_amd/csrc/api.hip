@@ -243,13 +243,16 @@ mla_status check_decode(const Resolved& r, const mla_decode_args* a) {
   return MLA_OK;
 }
 
+// latent: the absorbed query is given in args->q_nope ([B][n_q][h][d_c] fp32) and the
+// merged latent output goes to args->out ([B][n_q][h][d_c] fp32): no W_UK, W_UV or gate.
 mla_status decode_impl(const mla_dims* dims, const CacheRef& cache, const mla_decode_args* a,
-                       hipStream_t stream) {
+                       hipStream_t stream, bool latent = false) {
   Resolved r;
   mla_status st = resolve(dims, &r);
   if (st != MLA_OK) return st;
   st = check_decode(r, a);
   if (st != MLA_OK) return st;
+  if (latent && (r.dtype != MLA_BF16 || a->gate_x)) return MLA_E_UNSUPPORTED;
   Plan p{};
   if (r.dtype == MLA_BF16) p = plan_bf16(r, a);
   const Workspace ws = layout_ws(r, a, &p);
@@ -258,7 +261,7 @@ mla_status decode_impl(const mla_dims* dims, const CacheRef& cache, const mla_de
     return MLA_OK;
   }
   if (*a->workspace_bytes < ws.total) return MLA_E_WORKSPACE;
-  if (!cache.data || !a->kv_lens || !a->q_nope || !a->packed_w || !a->out) return MLA_E_NULL;
+  if (!cache.data || !a->kv_lens || !a->q_nope || (!a->packed_w && !latent) || !a->out) return MLA_E_NULL;
   if (r.d_r > 0 && !a->q_rope) return MLA_E_NULL;
   char* wsb = static_cast<char*>(a->workspace);
   const int M = a->batch * a->n_q;
@@ -293,8 +296,8 @@ mla_status decode_impl(const mla_dims* dims, const CacheRef& cache, const mla_de
     return launch_decode_f32(f, a->ev_attn_begin, a->ev_attn_end, stream) == hipSuccess ? MLA_OK : MLA_E_HIP;
   }
 
-  const uint16_t* w_uk_pk = static_cast<const uint16_t*>(a->packed_w);
-  const uint16_t* w_uv_pk = w_uk_pk + static_cast<size_t>(r.h) * 8192 * 8;
+  const uint16_t* w_uk_pk = latent ? nullptr : static_cast<const uint16_t*>(a->packed_w);
+  const uint16_t* w_uv_pk = latent ? nullptr : w_uk_pk + static_cast<size_t>(r.h) * 8192 * 8;
   // grids: the pairs a list may hold x head groups, padded to a multiple of 8 (one
   // run of units per XCD; the extra workgroups find no pair and return)
   auto grid_units = [](int64_t pairs, int groups) -> int64_t {
@@ -315,12 +318,13 @@ mla_status decode_impl(const mla_dims* dims, const CacheRef& cache, const mla_de
   q.kv_lens = a->kv_lens;
   q.q_cat = reinterpret_cast<uint16_t*>(wsb + ws.q_cat);
   q.q_lo = p.prec_pairs > 0 ? reinterpret_cast<uint16_t*>(wsb + ws.q_lo) : nullptr;
+  q.q_abs = latent ? static_cast<const float*>(a->q_nope) : nullptr;
   q.M = M;
   q.n_q = a->n_q;
   q.h = r.h;
   q.d_r = r.d_r;
   q.max_kv_len = a->max_kv_len;
-  q.out = a->out;  // zeroed here: the combine adds its two latent halves into it
+  q.out = latent ? nullptr : a->out;  // zeroed here: the combine adds its two latent halves into it
   q.qscale = qscale;
   for (int k = 0; k < r.d_r / 2 && k < 32; ++k) q.inv_freq[k] = pow(r.rope_base, -2.0 * k / r.d_r);
   q.plan.kv_lens = a->kv_lens;
@@ -386,7 +390,8 @@ mla_status decode_impl(const mla_dims* dims, const CacheRef& cache, const mla_de
   c.seq_off = q.plan.seq_off;
   c.w_uv_pk = w_uv_pk;
   c.gate = a->gate_x ? reinterpret_cast<const float*>(wsb + ws.gate) : nullptr;
-  c.out = a->out;
+  c.out = latent ? nullptr : a->out;
+  c.o_lat = latent ? a->out : nullptr;
   c.lse = a->lse;
   c.batch = a->batch;
   c.n_q = a->n_q;
@@ -486,6 +491,20 @@ mla_status mla_decode_paged(const mla_dims* dims, const void* pool, const int32_
   if (args && args->workspace && !block_table) return MLA_E_NULL;
   CacheRef c{pool, block_table, 0, block_size, max_blocks, n_blocks};
   return decode_impl(dims, c, args, stream);
+}
+
+mla_status mla_decode_latent(const mla_dims* dims, const void* cache, const mla_cache_layout* layout,
+                             const mla_decode_args* args, hipStream_t stream) {
+  if (!layout || !args) return MLA_E_NULL;
+  CacheRef c{cache, layout->block_table, layout->t_max, layout->block_size, layout->max_blocks, layout->n_blocks};
+  if (layout->block_table) {
+    if (layout->block_size <= 0 || layout->block_size % kTile != 0 || layout->max_blocks <= 0 || layout->n_blocks <= 0)
+      return MLA_E_SHAPE;
+    if (static_cast<int64_t>(layout->max_blocks) * layout->block_size < args->max_kv_len) return MLA_E_SHAPE;
+  } else if (layout->t_max <= 0 || layout->t_max < args->max_kv_len) {
+    return MLA_E_SHAPE;
+  }
+  return decode_impl(dims, c, args, stream, true);
 }
 
 mla_status mla_decode_noalloc(const mla_dims* dims, const void* cache, const mla_cache_layout* layout,

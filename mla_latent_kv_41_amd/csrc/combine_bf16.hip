@@ -54,7 +54,7 @@ __global__ __launch_bounds__(kWaves * 64) void combine_kernel(CombineArgs a) {
 
   // W_UV_i fragments of wave w's 32 output columns, 16 k-steps of half kh
   u32x4 bfr[16];
-  if (w < 4) {
+  if (w < 4 && !a.o_lat) {
     const u32x4* wv = reinterpret_cast<const u32x4*>(a.w_uv_pk) + ((static_cast<int64_t>(i) * 4 + w) * 32 + 16 * kh) * 64 + l;
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) bfr[ks] = wv[ks * 64];
@@ -128,6 +128,10 @@ __global__ __launch_bounds__(kWaves * 64) void combine_kernel(CombineArgs a) {
           o += wu * q[u];
         }
       }
+      if (a.o_lat) {  // latent mode: the merged latent half row is the output
+        *reinterpret_cast<f32x4*>(a.o_lat + (static_cast<int64_t>(m0 + r) * a.h + i) * 512 + kHalf * kh + 4 * l) = o;
+        continue;
+      }
       // o_lat as a hi + lo pair of bf16 (hi = bf16(o), lo = bf16(o - hi))
       hv = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
       lv = u32x2{pack_bf16x2(o[0] - __uint_as_float(hv[0] << 16), o[1] - __uint_as_float(hv[0] & 0xFFFF0000u)),
@@ -137,6 +141,7 @@ __global__ __launch_bounds__(kWaves * 64) void combine_kernel(CombineArgs a) {
     *(lds_u32x2*)(lds_ptr(s_hi) + r * kAStride + l * 8) = hv;
     *(lds_u32x2*)(lds_ptr(s_lo) + r * kAStride + l * 8) = lv;
   }
+  if (a.o_lat) return;  // uniform: no up-projection in latent mode
   __syncthreads();
   if (w >= 4) return;
 

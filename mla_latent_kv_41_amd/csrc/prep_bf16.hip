@@ -202,7 +202,7 @@ __global__ __launch_bounds__(512) void qprep_kernel(QPrepArgs a) {
     }
     // zero the output rows m = nb (mod 8) of these heads (the combine adds into them)
     const int per_row = nh * 32;  // float4 per row of this head group
-    for (int idx = st; idx < srows * per_row; idx += 64 * kQHeads) {
+    for (int idx = st; a.out && idx < srows * per_row; idx += 64 * kQHeads) {
       const int m = nb + kQColBlocks * (idx / per_row), q = idx % per_row;
       *reinterpret_cast<f32x4*>(a.out + (static_cast<int64_t>(m) * a.h + i0) * 128 + 4 * q) = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -223,33 +223,57 @@ __global__ __launch_bounds__(512) void qprep_kernel(QPrepArgs a) {
                         : u32x4{0u, 0u, 0u, 0u};
     }
   };
+  // latent mode: the absorbed query is given; its columns 64nb .. 64nb + 63 of head hw
+  // enter the staging below in the product's lane layout (row l%32, columns
+  // 32cb + 8j + 4(l/32) .. + 3 in values 4j .. 4j + 3)
+  const bool given = a.q_abs != nullptr;
+  auto load_given = [&](int mb, f32x16* acc) __attribute__((always_inline)) {
+    const int m = 32 * mb + (l & 31);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (m < a.M)
+          v = *reinterpret_cast<const f32x4*>(a.q_abs + (static_cast<int64_t>(m) * a.h + hw) * 512 + 64 * nb +
+                                              32 * cb + 8 * j + 4 * (l >> 5));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[cb][4 * j + e] = v[e];
+      }
+  };
   // the first block's rows go out before the weights, so they land first and the
   // products can follow the weights as they arrive
-  load_rows(0);
+  if (!given) load_rows(0);
   // W_UK fragments of head hw: column blocks 2nb, 2nb + 1, 8 k-steps each
   u32x4 bfr[2][8];
+  if (!given) {
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const u32x4* wk = reinterpret_cast<const u32x4*>(a.w_uk_pk) + ((static_cast<int64_t>(hw) * 16 + 2 * nb + cb) * 8) * 64 + l;
+    for (int cb = 0; cb < 2; ++cb) {
+      const u32x4* wk = reinterpret_cast<const u32x4*>(a.w_uk_pk) + ((static_cast<int64_t>(hw) * 16 + 2 * nb + cb) * 8) * 64 + l;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) bfr[cb][ks] = wk[ks * 64];
+      for (int ks = 0; ks < 8; ++ks) bfr[cb][ks] = wk[ks * 64];
+    }
   }
   __builtin_amdgcn_sched_barrier(0);  // every weight load issued before the rows' wait
   for (int mb = 0; mb * 32 < a.M; ++mb) {
-    if (mb > 0) load_rows(mb);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *(lds_u32x4*)(lds_ptr(area) + (4 * i + (l >> 4)) * kQnB + (l & 15) * 16) = rows[i];
-    // B fragment k-step ks: row l%32, k = 16ks + 8(l/32) + e
-    u32x4 af[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) af[ks] = *(lds_u32x4*)(lds_ptr(area) + (l & 31) * kQnB + (2 * ks + (l >> 5)) * 16);
     f32x16 acc[2];
+    if (given) {
+      load_given(mb, acc);
+    } else {
+      if (mb > 0) load_rows(mb);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      acc[cb] = f32x16{};
+      for (int i = 0; i < 8; ++i) *(lds_u32x4*)(lds_ptr(area) + (4 * i + (l >> 4)) * kQnB + (l & 15) * 16) = rows[i];
+      // B fragment k-step ks: row l%32, k = 16ks + 8(l/32) + e
+      u32x4 af[8];
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(bfr[cb][ks]), as_bf16x8(af[ks]), acc[cb], 0, 0, 0);
+      for (int ks = 0; ks < 8; ++ks) af[ks] = *(lds_u32x4*)(lds_ptr(area) + (l & 31) * kQnB + (2 * ks + (l >> 5)) * 16);
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        acc[cb] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+          acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(bfr[cb][ks]), as_bf16x8(af[ks]), acc[cb], 0, 0, 0);
+      }
     }
     // stage in the area (its fragments are in registers): lane l holds row l%32 and
     // columns 32cb + 8j + 4(l/32) + 0..3 in values 4j .. 4j+3; the high halves take

@@ -18,7 +18,8 @@ MLA_OK, MLA_E_NULL, MLA_E_SHAPE, MLA_E_DTYPE, MLA_E_UNSUPPORTED, MLA_E_WORKSPACE
 MLA_F32, MLA_BF16 = 0, 1
 
 EXPORTS = ("mla_absorb_weights", "mla_append_latent", "mla_decode", "mla_decode_paged",
-           "mla_decode_noalloc", "mla_expand_kv", "mla_decode_explicit", "mla_pack_down_weights",
+           "mla_decode_noalloc", "mla_decode_latent", "mla_expand_kv", "mla_decode_explicit",
+           "mla_pack_down_weights",
            "mla_project_append", "mla_status_string")
 
 
@@ -88,6 +89,9 @@ def lib():
         L.mla_decode_noalloc.restype = st
         L.mla_decode_noalloc.argtypes = [ctypes.POINTER(mla_dims), vp, ctypes.POINTER(mla_cache_layout),
                                          ctypes.POINTER(mla_decode_args), vp]
+        L.mla_decode_latent.restype = st
+        L.mla_decode_latent.argtypes = [ctypes.POINTER(mla_dims), vp, ctypes.POINTER(mla_cache_layout),
+                                        ctypes.POINTER(mla_decode_args), vp]
         L.mla_expand_kv.restype = st
         L.mla_expand_kv.argtypes = [ctypes.POINTER(mla_dims), vp, ctypes.POINTER(mla_cache_layout), ctypes.c_int32,
                                     vp, ctypes.c_int32, vp, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_size_t), vp]
@@ -336,6 +340,30 @@ def mla_decode_noalloc(d: mla_dims, cache, *, kv_lens, max_kv_len: int, q_nope, 
                             workspace_bytes=0, num_splits=num_splits, events=events)
     return _check(lib().mla_decode_noalloc(ctypes.byref(d), _ptr(cache), ctypes.byref(layout), ctypes.byref(a),
                                            _stream(stream)), "mla_decode_noalloc")
+
+
+def mla_decode_latent(d: mla_dims, cache, *, kv_lens, max_kv_len: int, q_abs, q_rope, o_lat, t_max: int = 0,
+                      block_table=None, block_size: int = 0, max_blocks: int = 0, n_blocks: int = 0,
+                      kv_lens_host: Optional[Sequence[int]] = None, lse=None, workspace=None,
+                      num_splits: int = 0, events=None, stream=None) -> int:
+    """Attention over the latent cache for an absorbed query given by the caller
+    (q_abs [B, n_q, h, d_c] fp32); writes the merged latent output o_lat [B, n_q, h, d_c]."""
+    B, n_q = q_abs.shape[0], q_abs.shape[1]
+    layout = mla_cache_layout(_ptr(block_table), t_max, block_size, max_blocks, n_blocks)
+    common = dict(batch=B, n_q=n_q, kv_lens=kv_lens, kv_lens_host=kv_lens_host, max_kv_len=max_kv_len,
+                  q_nope=q_abs, q_rope=q_rope, packed_w=None, gate_x=None, w_gate=None, out=o_lat, lse=lse,
+                  num_splits=num_splits, events=events)
+
+    def query():
+        a, n, _h = _decode_args(workspace=None, workspace_bytes=0, **common)
+        _check(lib().mla_decode_latent(ctypes.byref(d), _ptr(cache), ctypes.byref(layout), ctypes.byref(a), None),
+               "mla_decode_latent")
+        return n.value
+
+    ws = _workspace_for(query, workspace, q_abs.device)
+    a, n, _h = _decode_args(workspace=ws, workspace_bytes=ws.numel() * ws.element_size(), **common)
+    return _check(lib().mla_decode_latent(ctypes.byref(d), _ptr(cache), ctypes.byref(layout), ctypes.byref(a),
+                                          _stream(stream)), "mla_decode_latent")
 
 
 def mla_expand_kv(d: mla_dims, cache, *, kv_lens, max_kv_len: int, w_uk, w_uv, k_out, v_out, batch: int,

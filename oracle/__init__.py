@@ -199,6 +199,51 @@ def explicit_kv(*, c_kv, w_uk, w_uv, kv_lens, h: int, d_n: int, d_v: int):
     return K, V
 
 
+def latent_decode(*, q_abs, q_r, c_kv, k_r, kv_lens, scale: float, rope_base: float = 10000.0,
+                  store_bf16: bool = True):
+    """Attention in latent space for a given absorbed query, the step that weight-level
+    absorption leaves at run time (MLA tutorial page §2.2: W_UK absorbed into the
+    query's up-projection and W_UV into the output projection; §5.1: the scores
+    q_abs · c_KV and the weighted sum attn · c_KV stay in latent space; interview
+    guide §6.2 for the decoupled RoPE key). Per sequence b, query j (at position
+    p_j = kv_len - n_q + j) and head i:
+
+        s_t   = scale * (q_abs · c_t + RoPE(q_R, p_j) · k̃_R,t),  t <= p_j
+        o_lat = Σ_t softmax(s)_t c_t
+
+    ``q_abs [B, n_q, h, d_c]``, ``q_r [B, n_q, h, d_r]`` raw (or None), ``c_kv [B, T, d_c]``,
+    ``k_r [B, T, d_r]`` raw (or None); bf16 bits, float32 or float64. k̃_R is the rotated
+    key as the cache stores it (``cache_keys``). Returns fp64 ``o_lat [B, n_q, h, d_c]``
+    and ``lse [B, n_q, h]``."""
+    def f64(a):
+        if a is None:
+            return None
+        a = np.asarray(a)
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64) if a.dtype == np.uint16 \
+            else a.astype(np.float64)
+    qa, qr, c = f64(q_abs), f64(q_r), f64(c_kv)
+    B, n_q, h, d_c = qa.shape
+    d_r = 0 if qr is None else qr.shape[-1]
+    kr = cache_keys(d_r=d_r, k_r=k_r, kv_lens=kv_lens, rope_base=rope_base, store_bf16=store_bf16) if d_r else None
+    o_lat = np.full((B, n_q, h, d_c), np.nan)
+    lse = np.full((B, n_q, h), np.nan)
+    for b in range(B):
+        T = int(kv_lens[b])
+        for j in range(n_q):
+            pos = T - n_q + j
+            s = qa[b, j] @ c[b, :pos + 1].T                                   # [h, t]
+            if d_r:
+                qrot = np.stack([rope(qr[b, j, i], pos, rope_base) for i in range(h)])
+                s = s + qrot @ kr[b, :pos + 1].T
+            s = scale * s
+            m = s.max(axis=1, keepdims=True)
+            e = np.exp(s - m)
+            z = e.sum(axis=1, keepdims=True)
+            o_lat[b, j] = (e / z) @ c[b, :pos + 1]
+            lse[b, j] = (m + np.log(z))[:, 0]
+    return o_lat, lse
+
+
 def round_bf16_array(x) -> np.ndarray:
     """Nearest-even bf16 value of every element (fp64 in, fp64 out)."""
     x = np.ascontiguousarray(x, np.float64)

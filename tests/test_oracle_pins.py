@@ -540,3 +540,52 @@ def test_explicit_kv_attended_by_torch_equals_the_oracle():
     np.testing.assert_array_equal(K1[0, :4], c[0, :4].reshape(4, 2, 4))
     np.testing.assert_array_equal(V1[0, :4], c[0, :4].reshape(4, 2, 4))
     assert np.isnan(K1[0, 4]).all()
+
+
+def test_latent_decode_up_projected_equals_the_oracle():
+    """oracle.latent_decode with q_abs = q_nope · W_UK_iᵀ, its latent output then
+    multiplied by W_UV_i, equals the oracle's explicit form (1e-12): the two
+    absorption identities of the tutorial (§3.1) through independent code."""
+    w = synth.make_workload(4, batch=2, ctx_range=(30, 80))
+    t = synth.draw(w)
+    wuk = as_f64(t["w_uk"]).reshape(w.d_c, w.h, w.d_n)
+    wuv = as_f64(t["w_uv"]).reshape(w.d_c, w.h, w.d_v)
+    q_abs = np.einsum("bjhd,chd->bjhc", as_f64(t["q_nope"]), wuk)
+    o_lat, lse = oracle.latent_decode(q_abs=q_abs, q_r=t["q_r"], c_kv=t["c_kv"], k_r=t["k_r"], kv_lens=w.kv_lens,
+                                      scale=w.scale, store_bf16=False)
+    out = np.einsum("bjhc,chd->bjhd", o_lat, wuv).reshape(w.batch, w.n_q, -1)
+    ref, ref_lse = run_oracle(w, t, store_bf16=False, want_lse=True)
+    assert rel_err(out, ref) < 1e-12
+    assert np.max(np.abs(lse - ref_lse)) < 1e-10
+
+
+def test_weight_level_absorption_identity():
+    """Folding W_UK into the query's up-projection and W_UV into the output projection
+    (tutorial §2.2) changes nothing in exact arithmetic: with q_nope = c_Q · W_UQ and
+    y = out · W_O, the folded form c_Q · (W_UQ_i W_UK_iᵀ) -> latent attention ->
+    · (W_UV_i W_O_i) gives the same y (1e-12)."""
+    w = synth.make_workload(2, batch=2, ctx=60)
+    w.h = 4
+    t = synth.draw(w)
+    rng = np.random.default_rng(41)
+    d_q, d_model = 48, 40
+    c_q = rng.normal(size=(w.batch, w.n_q, d_q))
+    w_uq = rng.normal(size=(d_q, w.h * w.d_n)) / np.sqrt(d_q)
+    w_o = rng.normal(size=(w.h * w.d_v, d_model)) / np.sqrt(w.h * w.d_v)
+    wuk = as_f64(t["w_uk"]).reshape(w.d_c, w.h, w.d_n)
+    wuv = as_f64(t["w_uv"]).reshape(w.d_c, w.h, w.d_v)
+    f = lambda a: None if a is None else as_f64(a)
+    # the runtime form: the oracle's explicit decode between the two projections
+    q_nope = (c_q @ w_uq).reshape(w.batch, w.n_q, w.h, w.d_n)
+    out = oracle.mla_decode(h=w.h, d_c=w.d_c, d_r=w.d_r, d_n=w.d_n, d_v=w.d_v, c_kv=f(t["c_kv"]), k_r=f(t["k_r"]),
+                            kv_lens=w.kv_lens, q_nope=q_nope, q_r=f(t["q_r"]), w_uk=f(t["w_uk"]),
+                            w_uv=f(t["w_uv"]), store_bf16=False)
+    y_runtime = out @ w_o
+    # the folded form
+    w_uqk = np.einsum("qhd,chd->qhc", w_uq.reshape(d_q, w.h, w.d_n), wuk)          # [d_q, h, d_c]
+    w_uvo = np.einsum("chd,hdm->hcm", wuv, w_o.reshape(w.h, w.d_v, d_model))       # [h, d_c, d_model]
+    q_abs = np.einsum("bjq,qhc->bjhc", c_q, w_uqk)
+    o_lat, _ = oracle.latent_decode(q_abs=q_abs, q_r=f(t["q_r"]), c_kv=f(t["c_kv"]), k_r=f(t["k_r"]),
+                                    kv_lens=w.kv_lens, scale=w.scale, store_bf16=False)
+    y_folded = np.einsum("bjhc,hcm->bjm", o_lat, w_uvo)
+    assert rel_err(y_folded, y_runtime) < 1e-12
