@@ -71,14 +71,18 @@ typedef struct {
 /*
  * Supported shapes. MLA_F32: any h <= 1024, d_c <= 1024, d_rope <= 256 and even,
  * d_qk_nope <= 256, d_v <= 256 (a plain fp32 path for small layers).
- * MLA_BF16: d_c = 512, d_rope in {0, 64}, d_qk_nope = 128, d_v = 128, with
- * n_heads * n_q a multiple of 64, and n_q dividing each group of 128 query rows
- * (64 when n_heads * n_q is not a multiple of 128) into whole head groups (the
- * DeepSeek-V2/V3 attention shape and its position-free gated variant); with a gate, d_model a
- * multiple of 16 and n_heads a multiple of 4. Paged caches need block_size a
- * multiple of 32. Other shapes return MLA_E_UNSUPPORTED (or MLA_E_SHAPE).
+ * MLA_BF16: d_c = 512, d_rope in {0, 64}, d_qk_nope = 128, d_v = 128, n_heads a
+ * multiple of 32 with n_heads * n_q a multiple of 64 (the DeepSeek-V2/V3 attention
+ * shape and its position-free gated variant); with a gate, d_model a multiple of
+ * 256. Paged caches need block_size a multiple of 32. Other shapes return
+ * MLA_E_UNSUPPORTED (or MLA_E_SHAPE).
+ *
+ * Precision of the bf16 decode: the cache, weights and queries are bf16; products
+ * accumulate in fp32; the split partials and their merge are fp32; the absorbed,
+ * scaled query and the softmax probabilities enter the matrix cores as bf16 for
+ * sequences of 4096 tokens or more, and as hi + lo bf16 pairs (about 16 significant
+ * bits) for shorter sequences, where single bf16 roundings do not average out.
  */
-
 /*
  * One-time weight absorption / packing (tutorial §3.2: "preprocess the absorbed
  * weights once at load time"; the einsums `bhsd,hcd->bhsc` and `bhsc,hdc->bhsd`
