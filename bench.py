@@ -113,16 +113,17 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def traffic_from_profile(per_launch_units):
-    """HBM bytes per attention launch from the committed rocprofv3 counter runs,
-    or None when absent or taken on a different kernel source."""
+def traffic_from_profile(workload):
+    """HBM bytes of one step's attention launches for `workload` (a workload name)
+    from the committed rocprofv3 counter runs, or None when absent or taken on a
+    different kernel source."""
     p = os.path.join(ROOT, "profiles", "attention_traffic.json")
     if not os.path.exists(p):
         return None
-    d = json.load(open(p))
-    if d.get("kernel_source_sha256") != kernel_source_hash():
+    rec = json.load(open(p)).get("workloads", {}).get(workload)
+    if rec is None or rec.get("kernel_source_sha256") != kernel_source_hash():
         return None
-    return d.get("bytes_per_launch")
+    return rec.get("bytes_per_launch")
 
 
 def stream_read_gbps(nbytes=1 << 30, reps=10):
@@ -154,6 +155,49 @@ def _host_cores():
         return len(os.sched_getaffinity(0))
     except AttributeError:
         return os.cpu_count()
+
+
+GRAPH_ROUNDS = 10  # rounds over the COPIES cache copies captured in one graph
+
+
+def graph_step_ms(steps, n_steps):
+    """Step time with the host taken out: GRAPH_ROUNDS x COPIES decode steps (the same
+    rotation as the eager loop) captured into one HIP graph, replayed until about
+    n_steps steps have run. Before timing, the graph is replayed three times with an
+    eager step between replays, and each replay's output must equal the eager output
+    bit for bit (the merge order is fixed, so the step is deterministic). Returns
+    (ms per step, replays checked)."""
+    import torch
+    per_graph = GRAPH_ROUNDS * COPIES
+    out = steps[0].out
+    steps[0].decode()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for k in range(per_graph):
+            steps[k % COPIES].decode()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out, ref):
+            raise RuntimeError("graph replay differs from the eager step")
+        steps[1 % COPIES].decode()
+        torch.cuda.synchronize()
+    replays = max(3, -(-n_steps // per_graph))
+    g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(replays):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / (replays * per_graph)
+    del g
+    return ms, 3
 
 
 def cpu_baseline(w, t, budget_s=12.0):
@@ -221,8 +265,8 @@ TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out>/prof
              "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline")
 TRACE_CMD_CFG = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out>/prof_c{c} -o c{c} -- "
                  "python3 bench.py --config {c} --steps 10 --warmup 3 --no-cpu-baseline")
-PMC_CMD = ("rocprofv3 --pmc {c} --output-format csv -d <out>/pmc/{c} -o {c} -- "
-           "python3 bench.py --steps 4 --warmup 2 --no-cpu-baseline --calibrate-copy")
+PMC_CMD = ("rocprofv3 --pmc {c} --output-format csv -d <out>/pmc_c{cfg}/{c} -o {c} -- "
+           "python3 bench.py --config {cfg} --steps 4 --warmup 2 --no-cpu-baseline --calibrate-copy")
 COPY_BYTES = 512 << 20
 
 
@@ -337,28 +381,28 @@ def summarize_append_counters(d):
 
 
 def summarize_profiles(d):
-    """Summaries of a kernel-trace run (DIR/prof_ds, log DIR/prof_ds.log) and of one
-    FETCH_SIZE and one WRITE_SIZE counter run (DIR/pmc/<C>, logs DIR/pmc/<C>.log) of
-    this bench: the per-kernel table, the counter table with the 512 MiB copy
-    calibration, and profiles/attention_traffic.json, keyed by the attention kernel
-    source hash the profiled runs printed."""
-    import csv
-    import glob
-    from collections import defaultdict
-    prof = os.path.join(ROOT, "profiles")
+    """profiles/ summaries of whatever rocprofv3 output DIR holds: the fused append's
+    trace and counters, the DeepSeek-shaped kernel trace (DIR/prof_ds), the other
+    workloads' traces, their kernel-efficiency counters, and their HBM traffic
+    counters (one FETCH_SIZE and one WRITE_SIZE run per workload, with the 512 MiB
+    copy calibration) into profiles/attention_traffic.json, keyed by the attention
+    kernel source hash the profiled runs printed."""
     if os.path.isdir(os.path.join(d, "prof_append")):
         summarize_append_trace(d)
     if os.path.isdir(os.path.join(d, "pmc_append")):
         summarize_append_counters(d)
-    if not os.path.isdir(os.path.join(d, "prof_ds")):
-        return
+    if os.path.isdir(os.path.join(d, "prof_ds")):
+        summarize_ds_trace(d)
+    summarize_other(d)
+
+
+def summarize_ds_trace(d):
+    """profiles/ summary of the DeepSeek-shaped kernel trace (DIR/prof_ds)."""
+    import csv
+    import glob
+    prof = os.path.join(ROOT, "profiles")
     w_name = "deepseek_b32_ctx4096"
-    shas = {_bench_line(os.path.join(d, "prof_ds.log"))["attention_kernel_source_sha256"]}
-    for c in ("FETCH_SIZE", "WRITE_SIZE"):
-        shas.add(_bench_line(os.path.join(d, "pmc", c + ".log"))["attention_kernel_source_sha256"])
-    if len(shas) != 1:
-        raise SystemExit("profiled runs used different attention kernel sources: %s" % shas)
-    sha = shas.pop()
+    sha = _bench_line(os.path.join(d, "prof_ds.log"))["attention_kernel_source_sha256"]
 
     def short(name):
         name = name.replace("void ", "", 1)
@@ -383,53 +427,14 @@ def summarize_profiles(d):
     lines += ["", "Attention kernel source sha256 (mla_latent_kv_41_amd/csrc/decode_bf16.hip + common.hpp): `%s`" % sha, ""]
     open(os.path.join(prof, "decode_step_%s_kernel_trace.md" % w_name), "w").write("\n".join(lines))
 
-    vals = defaultdict(lambda: defaultdict(list))
-    for c in ("FETCH_SIZE", "WRITE_SIZE"):
-        for f in glob.glob(os.path.join(d, "pmc", c, "*counter_collection.csv")):
-            for r in csv.DictReader(open(f)):
-                vals[(short(r["Kernel_Name"]), int(r["Grid_Size"]))][r["Counter_Name"]].append(
-                    float(r["Counter_Value"]))
-    copy = [k for k in vals if "copyBuffer" in k[0] and k[1] == COPY_BYTES // 4096]
-    if len(copy) != 1:
-        raise SystemExit("calibration copy not found in the counter runs")
-    cf = {c: sum(v) / len(v) for c, v in vals[copy[0]].items()}
-    f_fac = COPY_BYTES / (cf["FETCH_SIZE"] * 1024)
-    w_fac = COPY_BYTES / (cf["WRITE_SIZE"] * 1024)
-    dec = [k for k in vals if k[0] == kname]
-    if len(dec) != 1:
-        raise SystemExit("attention kernel not found in the counter runs")
-    dv = {c: sum(v) / len(v) for c, v in vals[dec[0]].items()}
-    fetch_b = dv["FETCH_SIZE"] * 1024 * f_fac
-    write_b = dv["WRITE_SIZE"] * 1024 * w_fac
-    lines = ["# HBM traffic counters: %s, DeepSeek-shaped decode (h=128, B=32, 4096+1 tokens)" % kname, "",
-             "Commands (one counter per pass, from /tmp with TMPDIR=/tmp; `--calibrate-copy` adds one 512 MiB "
-             "device-to-device copy, dispatched as `__amd_rocclr_copyBuffer` with grid %d):" % (COPY_BYTES // 4096), ""]
-    lines += ["    " + PMC_CMD.format(c=c) for c in ("FETCH_SIZE", "WRITE_SIZE")]
-    lines += ["", "Summarised with `python3 bench.py --summarize-profiles <out>`.", "",
-              "Attention kernel source sha256 (mla_latent_kv_41_amd/csrc/decode_bf16.hip + common.hpp): `%s`" % sha, "",
-              "| kernel | grid | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB |", "|---|---|---|---|---|"]
-    for (n, g), cs in sorted(vals.items(), key=lambda kv: -sum(kv[1].get("FETCH_SIZE", [0])) / max(1, len(kv[1].get("FETCH_SIZE", [0])))):
-        fs = cs.get("FETCH_SIZE", [float("nan")])
-        ws = cs.get("WRITE_SIZE", [float("nan")])
-        lines.append("| `%s` | %d | %d | %.1f | %.1f |" % (n, g, len(fs), sum(fs) / len(fs), sum(ws) / len(ws)))
-    lines += ["", "Calibration: the 512 MiB copy reads and writes %d bytes; FETCH_SIZE counts %.1f KiB "
-              "(factor %.4f bytes per counted byte) and WRITE_SIZE %.1f KiB (factor %.4f)." % (
-                  COPY_BYTES, cf["FETCH_SIZE"], f_fac, cf["WRITE_SIZE"], w_fac), "",
-              "%s per launch: fetch %.1f MB, write %.1f MB, total %.1f MB." % (
-                  kname, fetch_b / 1e6, write_b / 1e6, (fetch_b + write_b) / 1e6), ""]
-    open(os.path.join(prof, "attention_%s_hbm_counters.md" % w_name), "w").write("\n".join(lines))
-    rec = {"kernel": kname, "workload": w_name, "kernel_source_sha256": sha,
-           "kernel_sources": ["mla_latent_kv_41_amd/csrc/" + f for f in KERNEL_SOURCES],
-           "fetch_size_kib_per_dispatch": round(dv["FETCH_SIZE"], 1),
-           "write_size_kib_per_dispatch": round(dv["WRITE_SIZE"], 1),
-           "copy_calibration": {"bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
-                                "fetch_size_kib": cf["FETCH_SIZE"], "write_size_kib": cf["WRITE_SIZE"],
-                                "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4)},
-           "fetch_bytes_per_launch": int(fetch_b), "write_bytes_per_launch": int(write_b),
-           "bytes_per_launch": int(fetch_b + write_b)}
-    json.dump(rec, open(os.path.join(prof, "attention_traffic.json"), "w"), indent=1)
-    # kernel traces of the other workloads, where DIR holds them (DIR/prof_c<N>, log
-    # DIR/prof_c<N>.log)
+
+def summarize_other(d):
+    """Kernel traces of the other workloads (DIR/prof_c<N>, log DIR/prof_c<N>.log),
+    kernel-efficiency counters (DIR/ctr_c<N>) and HBM traffic counters (DIR/pmc_c<N>)."""
+    import csv
+    import glob
+    prof = os.path.join(ROOT, "profiles")
+    short = _short_kernel_name
     for c in (3, 4, 5):
         tdir = os.path.join(d, "prof_c%d" % c)
         if not os.path.isdir(tdir):
@@ -452,7 +457,86 @@ def summarize_profiles(d):
     for c in (2, 3, 4, 5):
         if os.path.isdir(os.path.join(d, "ctr_c%d" % c, "sq")):
             summarize_efficiency_counters(d, c)
-    print("summaries written for attention kernel source %s" % sha)
+        if os.path.isdir(os.path.join(d, "pmc_c%d" % c, "WRITE_SIZE")):
+            summarize_traffic(d, c)
+    print("summaries written")
+
+
+def summarize_traffic(d, cfg):
+    """HBM traffic of one workload's attention launches from one FETCH_SIZE and one
+    WRITE_SIZE counter run (DIR/pmc_c<cfg>/<C>, logs DIR/pmc_c<cfg>/<C>.log), scaled by
+    what the same counters read for the 512 MiB calibration copy of the same run:
+    profiles/attention_<workload>_hbm_counters.md and the workload's entry in
+    profiles/attention_traffic.json, keyed by the attention kernel source hash."""
+    import csv
+    import glob
+    from collections import defaultdict
+    prof = os.path.join(ROOT, "profiles")
+    base = os.path.join(d, "pmc_c%d" % cfg)
+    lines_of = {c: _bench_line(os.path.join(base, c + ".log")) for c in ("FETCH_SIZE", "WRITE_SIZE")}
+    shas = {ln["attention_kernel_source_sha256"] for ln in lines_of.values()}
+    if len(shas) != 1:
+        raise SystemExit("counter runs used different attention kernel sources: %s" % shas)
+    sha = shas.pop()
+    wl = lines_of["FETCH_SIZE"]["config"]["workload"]
+    vals = defaultdict(lambda: defaultdict(list))
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        for f in glob.glob(os.path.join(base, c, "*counter_collection.csv")):
+            for r in csv.DictReader(open(f)):
+                vals[(_short_kernel_name(r["Kernel_Name"]), int(r["Grid_Size"]))][r["Counter_Name"]].append(
+                    float(r["Counter_Value"]))
+    copy = [k for k in vals if "copyBuffer" in k[0] and k[1] == COPY_BYTES // 4096]
+    if len(copy) != 1:
+        raise SystemExit("calibration copy not found in the counter runs")
+    cf = {c: sum(v) / len(v) for c, v in vals[copy[0]].items()}
+    f_fac = COPY_BYTES / (cf["FETCH_SIZE"] * 1024)
+    w_fac = COPY_BYTES / (cf["WRITE_SIZE"] * 1024)
+    attn = sorted(k for k in vals if k[0].startswith(ATTENTION_KERNELS))
+    if not attn:
+        raise SystemExit("no attention kernel in the counter runs of config %d" % cfg)
+    names = sorted({k[0] for k in attn})
+    if len(attn) != len(names):
+        raise SystemExit("an attention kernel ran with several grids: %s" % attn)
+    avg = {k: {c: sum(v) / len(v) for c, v in vals[k].items()} for k in attn}
+    fetch_b = sum(v["FETCH_SIZE"] for v in avg.values()) * 1024 * f_fac
+    write_b = sum(v["WRITE_SIZE"] for v in avg.values()) * 1024 * w_fac
+    kname = " + ".join(names)
+    lines = ["# HBM traffic counters: attention launches of %s (`bench.py --config %d`)" % (wl, cfg), "",
+             "Commands (one counter per pass, from /tmp with TMPDIR=/tmp; `--calibrate-copy` adds one 512 MiB "
+             "device-to-device copy, dispatched as `__amd_rocclr_copyBuffer` with grid %d):" % (COPY_BYTES // 4096), ""]
+    lines += ["    " + PMC_CMD.format(c=c, cfg=cfg) for c in ("FETCH_SIZE", "WRITE_SIZE")]
+    lines += ["", "Summarised with `python3 bench.py --summarize-profiles <out>`.", "",
+              "Attention kernel source sha256 (mla_latent_kv_41_amd/csrc/decode_bf16.hip + common.hpp): `%s`" % sha, "",
+              "| kernel | grid | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB |", "|---|---|---|---|---|"]
+    for (n, g), cs in sorted(vals.items(), key=lambda kv: -sum(kv[1].get("FETCH_SIZE", [0])) / max(1, len(kv[1].get("FETCH_SIZE", [0])))):
+        fs = cs.get("FETCH_SIZE", [float("nan")])
+        ws = cs.get("WRITE_SIZE", [float("nan")])
+        lines.append("| `%s` | %d | %d | %.1f | %.1f |" % (n, g, len(fs), sum(fs) / len(fs), sum(ws) / len(ws)))
+    alg = lines_of["FETCH_SIZE"]["roofline"]["algorithmic_bytes_per_launch"]
+    lines += ["", "Calibration: the 512 MiB copy reads and writes %d bytes; FETCH_SIZE counts %.1f KiB "
+              "(factor %.4f bytes per counted byte) and WRITE_SIZE %.1f KiB (factor %.4f)." % (
+                  COPY_BYTES, cf["FETCH_SIZE"], f_fac, cf["WRITE_SIZE"], w_fac), "",
+              "Attention launches of one step (%s): fetch %.1f MB, write %.1f MB, total %.1f MB, against %.1f MB "
+              "algorithmic (%.2fx)." % (kname, fetch_b / 1e6, write_b / 1e6, (fetch_b + write_b) / 1e6, alg / 1e6,
+                                       (fetch_b + write_b) / alg), ""]
+    open(os.path.join(prof, "attention_%s_hbm_counters.md" % wl), "w").write("\n".join(lines))
+    p = os.path.join(prof, "attention_traffic.json")
+    doc = json.load(open(p)) if os.path.exists(p) else {}
+    doc = doc if "workloads" in doc else {"workloads": {}}
+    doc["workloads"][wl] = {
+        "kernels": names, "kernel_source_sha256": sha,
+        "kernel_sources": ["mla_latent_kv_41_amd/csrc/" + f for f in KERNEL_SOURCES],
+        "fetch_size_kib_per_step": round(sum(v["FETCH_SIZE"] for v in avg.values()), 1),
+        "write_size_kib_per_step": round(sum(v["WRITE_SIZE"] for v in avg.values()), 1),
+        "copy_calibration": {"bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+                             "fetch_size_kib": cf["FETCH_SIZE"], "write_size_kib": cf["WRITE_SIZE"],
+                             "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4)},
+        "fetch_bytes_per_launch": int(fetch_b), "write_bytes_per_launch": int(write_b),
+        "bytes_per_launch": int(fetch_b + write_b), "algorithmic_bytes_per_launch": alg}
+    json.dump(doc, open(p, "w"), indent=1)
+    print("traffic counters written for %s" % wl)
+
+
 
 
 ATTENTION_KERNELS = ("mla::decode_kernel", "mla::decode_roles_kernel")
@@ -953,7 +1037,7 @@ def main():
     cache_gbps = cache_bytes / (ms * 1e-3) / 1e9
     tok_s = w.batch * w.n_q / (ms * 1e-3)
     attn_gbps = cache_bytes / (attn_avg * 1e-3) / 1e9
-    traffic = traffic_from_profile(1) if args.config == 2 else None
+    traffic = traffic_from_profile(w.name)
     attn_flops = attention_flops(w)
     attn_tflops = attn_flops / (attn_avg * 1e-3) / 1e12
     mfma_bound = args.config == 4  # 256 score rows per tile: the matrix cores bind
@@ -996,6 +1080,12 @@ def main():
         "attention_kernel_source_sha256": kernel_source_hash(),
         "roofline": roof,
     }
+    # the same steps replayed from a HIP graph (no Python or launch overhead): the
+    # difference to ms_per_step is what the host adds per step
+    g_ms, g_checked = graph_step_ms(steps, args.steps)
+    out["graph_ms_per_step"] = round(g_ms, 5)
+    out["graph_replays_checked_bitwise"] = g_checked
+    out["host_overhead_ms_per_step"] = round(ms - g_ms, 5)
     if not args.no_cpu_baseline:
         out["stream_read_GBps"] = stream_read_gbps()
         out["attention_frac_of_stream_read"] = round(attn_gbps / out["stream_read_GBps"], 4)

@@ -49,5 +49,5 @@ def test_fused_append_units():
 def test_committed_traffic_records_match_the_sources():
     """The counter records in profiles/ carry the hash of the kernel sources they
     were measured on; while it matches, the bench reports their traffic."""
-    assert bench.traffic_from_profile(1) is not None, "attention counters are stale"
+    assert bench.traffic_from_profile("deepseek_b32_ctx4096") is not None, "attention counters are stale"
     assert bench.append_traffic_from_profile() is not None, "fused-append counters are stale"
