@@ -78,7 +78,7 @@ struct Plan {
   int chunk_precise; // ... of the precise form's sequences
   int64_t cap;       // pairs the workspace holds: a bound on Σ_b ceil(kv_b / chunk)
   int64_t fast_pairs, prec_pairs;  // bounds on the pairs of each list (0: not launched)
-  int comb_rows;     // combine: query rows per workgroup (<= 32)
+  int comb_rows;     // combine: query rows per workgroup (16, 8, 4, 2 or 1)
 };
 
 int64_t ceil_div(int64_t x, int64_t y) { return (x + y - 1) / y; }
@@ -167,11 +167,11 @@ Plan plan_bf16(const Resolved& r, const mla_decode_args* a) {
     p.fast_pairs = L >= kPreciseBelow ? p.cap : 0;
     p.prec_pairs = p.cap;
   }
-  // combine grid: (h, 2 latent halves, M / rows): halve the rows until the grid has
-  // a workgroup per CU
+  // combine grid: (h, M / rows), rows 16, 8, 4, 2 or 1: halved until the grid has a
+  // workgroup per CU
   const int M = a->batch * a->n_q;
-  p.comb_rows = std::min(32, M);
-  while (p.comb_rows > 1 && 2LL * r.h * ceil_div(M, p.comb_rows) < target) p.comb_rows = (p.comb_rows + 1) / 2;
+  p.comb_rows = 16;
+  while (p.comb_rows > 1 && static_cast<int64_t>(r.h) * ceil_div(M, p.comb_rows) < target) p.comb_rows /= 2;
   return p;
 }
 
@@ -324,7 +324,6 @@ mla_status decode_impl(const mla_dims* dims, const CacheRef& cache, const mla_de
   q.h = r.h;
   q.d_r = r.d_r;
   q.max_kv_len = a->max_kv_len;
-  q.out = latent ? nullptr : a->out;  // zeroed here: the combine adds its two latent halves into it
   q.qscale = qscale;
   for (int k = 0; k < r.d_r / 2 && k < 32; ++k) q.inv_freq[k] = pow(r.rope_base, -2.0 * k / r.d_r);
   q.plan.kv_lens = a->kv_lens;

@@ -7,7 +7,8 @@
 //   lse = (M + log2 L) ln 2 (natural-log units).
 // Up-projection (MLA tutorial page §3.1 and the `bhsc,hdc->bhsd` einsum of §5.1):
 // out[m, i*128 + d] = o_lat[m, i, :] · W_UV_i[:, d], on v_mfma_f32_32x32x16_bf16
-// with o_lat entering as a hi + lo pair of bf16 rows (about 16 significant bits).
+// with o_lat entering as a hi + lo pair of bf16 rows (about 16 significant bits),
+// stored once per output element.
 // Gate (Gated-MLA page §2.6): out *= sigmoid(g), g = x · W_G per channel of the
 // concatenated heads.
 #include "common.hpp"
@@ -16,167 +17,221 @@
 namespace mla {
 
 namespace {
-constexpr int kGateSplit = 16;             // K-splits of the gate GEMM
-constexpr int kHalf = 256;                 // latent columns per workgroup (half of d_c)
-constexpr int kAStride = kHalf * 2 + 16;   // bytes per o_lat half row in LDS (padded)
-constexpr int kBatch = 8;                  // partial half rows per row in flight at once
-constexpr int kWaves = 8;                  // waves per workgroup
-constexpr int kRowsPerWave = 4;            // query rows per wave (32 per workgroup)
+constexpr int kGateSplit = 16;            // K-splits of the gate GEMM
+constexpr int kWaves = 8;                 // waves per workgroup
+constexpr int kMaxRows = 16;              // query rows per workgroup
+constexpr int kAStride = 512 * 2 + 16;    // bytes per merged row in LDS (512 bf16, padded)
+
+template <int N>
+struct VecT {
+  typedef float T __attribute__((ext_vector_type(N)));
+};
+template <>
+struct VecT<1> {
+  typedef float T;
+};
+
+// the N bf16 halves of N floats, packed into N / 2 words (N = 1: the low half of one)
+template <int N>
+__device__ __forceinline__ void to_bf16_pair(const float (&x)[N], uint32_t (&hi)[(N + 1) / 2], uint32_t (&lo)[(N + 1) / 2]) {
+#pragma unroll
+  for (int k = 0; k < (N + 1) / 2; ++k) {
+    const float x0 = x[2 * k], x1 = 2 * k + 1 < N ? x[2 * k + 1] : 0.f;
+    hi[k] = pack_bf16x2(x0, x1);
+    lo[k] = pack_bf16x2(x0 - __uint_as_float(hi[k] << 16), x1 - __uint_as_float(hi[k] & 0xFFFF0000u));
+  }
+}
 }  // namespace
 
-// grid (h, 2, ceil(M / R)), 512 threads, R <= 32 query rows per workgroup. Workgroup
-// (i, kh, mb) takes head i, latent columns [256 kh, 256 kh + 256) and query rows
-// m0 .. m0 + R - 1, and adds its share of the up-projection,
-//   out[m][i*128 + d] += Σ_{c in half kh} o_lat[m][i][c] · W_UV_i[c][d],
-// into the output with fp32 atomics (the output was zeroed by the query preparation
-// of the same call). Each output element gets exactly two addends onto zero, so the
-// sum does not depend on their order. Splitting the latent dimension, not the rows,
-// reads each partial row and each W_UV_i once.
+// grid (h, ceil(M / R)), 512 threads; R = rows_per_wg in {16, 8, 4, 2, 1} query rows.
+// Workgroup (i, mb) merges query rows m0 .. m0 + R - 1 of head i over all 512 latent
+// columns and writes their up-projection
+//   out[m][i*128 + d] = Σ_c o_lat[m][i][c] · W_UV_i[c][d]
+// with plain stores: every output element has one writer, so the output needs no
+// clearing and the result does not depend on timing.
 //
-// Sequence b's ranges hold partial indices seq_off[b] .. seq_off[b + 1] - 1 (the
-// plan's compact layout). Wave w takes rows w, w + 8, w + 16, w + 24, lane l columns
-// 4l .. 4l + 3 of the half row. Everything a wave needs goes out at once: the (m, l)
-// of each row's first 64 ranges (lane s: range s) and the half rows of its first 8
-// ranges, so a wave waits for memory about once. Lane s then forms range s's weight
-// 2^(m_s - M) / L, which the merge reads back with readlane; further ranges come 8
-// at a time. Ranges merge in a fixed order, so the result is deterministic. Waves
-// 0-3 also load the W_UV_i fragments first and run the up-projection.
+// Merge. The statistics of a row are formed by whole waves: WPR = 8 / R waves share
+// a row when R < 8, each taking 512 / WPR columns (VW = 8 / WPR per lane); with R = 8
+// or 16 each wave takes one or two rows (columns 8l .. 8l + 7 per lane). Sequence b's
+// ranges hold partial indices seq_off[b] .. seq_off[b + 1] - 1. Lane s reads range
+// s's (m, l) (ranges past 64 in a loop), wave reductions give M and L, lane s forms
+// the weight 2^(m_s - M) / L, and the merge reads the weights back with readlane.
+// The first NB partial rows of every row go out at once, further ones NB at a time;
+// ranges merge in a fixed order.
+//
+// Up-projection, on v_mfma_f32_32x32x16_bf16: the merged rows enter as hi + lo pairs
+// of bf16 rows from LDS (rows past the workgroup's read as zeros). Wave w computes the
+// 32 output columns of block w % 4 over latent half w / 4 (its 16 W_UV_i fragments
+// are loaded first); waves 4-7 hand their sums to waves 0-3 through LDS, which add
+// them, apply the gate and store.
+template <int WPR>
 __global__ __launch_bounds__(kWaves * 64) void combine_kernel(CombineArgs a) {
-  __shared__ __attribute__((aligned(16))) char s_hi[32 * kAStride];
-  __shared__ __attribute__((aligned(16))) char s_lo[32 * kAStride];
-  const int i = blockIdx.x, kh = blockIdx.y, mb = blockIdx.z;
+  constexpr int VW = 8 / WPR;              // floats per lane of a row
+  constexpr int RPW = WPR == 1 ? 2 : 1;    // row slots per wave
+  constexpr int NB = WPR == 1 ? 4 : 8;     // partial rows per row in flight
+  using V = typename VecT<VW>::T;
+  __shared__ __attribute__((aligned(16))) char s_hi[kMaxRows * kAStride];
+  __shared__ __attribute__((aligned(16))) char s_lo[kMaxRows * kAStride];
+  __shared__ __attribute__((aligned(16))) float s_x[4][8][64];
+  const int i = blockIdx.x, mb = blockIdx.y;
   const int tid = threadIdx.x, l = tid % 64;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64);
   const int M = a.batch * a.n_q;
-  const int m0 = mb * a.rows_per_wg;
-  const int rows = min(a.rows_per_wg, M - m0);
+  const int R = a.rows_per_wg;
+  const int m0 = mb * R;
+  const int rows = min(R, M - m0);
   const int64_t rstride = static_cast<int64_t>(a.n_q) * a.h;  // partial rows per range
+  const bool latent = a.o_lat != nullptr;
+  const int cb = w & 3, kh = w >> 2;
 
-  // W_UV_i fragments of wave w's 32 output columns, 16 k-steps of half kh
+  // W_UV_i fragments of column block cb, the 16 k-steps of latent half kh
   u32x4 bfr[16];
-  if (w < 4 && !a.o_lat) {
-    const u32x4* wv = reinterpret_cast<const u32x4*>(a.w_uv_pk) + ((static_cast<int64_t>(i) * 4 + w) * 32 + 16 * kh) * 64 + l;
+  if (!latent) {
+    const u32x4* wv = reinterpret_cast<const u32x4*>(a.w_uv_pk) + ((static_cast<int64_t>(i) * 4 + cb) * 32 + 16 * kh) * 64 + l;
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) bfr[ks] = wv[ks * 64];
   }
 
-  // this wave's rows: (first partial row, number of ranges)
-  int64_t row0[kRowsPerWave];
-  int ns[kRowsPerWave];
+  // this wave's rows and columns
+  const int sub = WPR == 1 ? 0 : w % WPR;
+  const int col0 = sub * (512 / WPR) + VW * l;
+  int rr[RPW], ns[RPW];
+  int64_t row0[RPW];
 #pragma unroll
-  for (int k = 0; k < kRowsPerWave; ++k) {
-    const int r = w + kWaves * k;
+  for (int k = 0; k < RPW; ++k) {
+    rr[k] = WPR == 1 ? w + kWaves * k : w / WPR;
     ns[k] = 0;
     row0[k] = 0;
-    if (r < rows) {  // uniform
-      const int m = m0 + r, b = m / a.n_q, j = m - b * a.n_q;
+    if (rr[k] < rows) {  // uniform
+      const int m = m0 + rr[k], b = m / a.n_q, j = m - b * a.n_q;
       const int p0 = a.seq_off[b];
       ns[k] = a.seq_off[b + 1] - p0;
       row0[k] = (static_cast<int64_t>(p0) * a.n_q + j) * a.h + i;
     }
   }
-  // (m, l) of ranges l (< 64) and the first kBatch half rows of every row
-  f32x2 ml[kRowsPerWave];
-  f32x4 v[kRowsPerWave][kBatch];
+  // (m, l) of ranges l (< 64) and the first NB partial rows of every row
+  f32x2 ml[RPW];
+  V v[RPW][NB];
 #pragma unroll
-  for (int k = 0; k < kRowsPerWave; ++k) {
-    ml[k] = l < ns[k] ? *reinterpret_cast<const f32x2*>(a.ml_part + (row0[k] + l * rstride) * 2)
-                      : f32x2{-INFINITY, 0.f};
-    const float* src = a.o_part + row0[k] * 512 + kHalf * kh + 4 * l;
+  for (int k = 0; k < RPW; ++k) {
+    ml[k] = l < ns[k] ? *reinterpret_cast<const f32x2*>(a.ml_part + (row0[k] + l * rstride) * 2) : f32x2{-INFINITY, 0.f};
+    const float* src = a.o_part + row0[k] * 512 + col0;
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u)
-      v[k][u] = u < ns[k] ? *reinterpret_cast<const f32x4*>(src + u * rstride * 512) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < NB; ++u) v[k][u] = u < ns[k] ? *reinterpret_cast<const V*>(src + u * rstride * 512) : V{};
   }
 
 #pragma unroll
-  for (int k = 0; k < kRowsPerWave; ++k) {
-    const int r = w + kWaves * k;
-    if (r >= 32) break;
-    u32x2 hv = {0u, 0u}, lv = {0u, 0u};
-    if (r < rows) {  // uniform
-      // ---- statistics over the ranges (ranges past 64 in a loop)
-      float mx = ml[k][0];
-      for (int s = l + 64; s < ns[k]; s += 64) mx = fmaxf(mx, a.ml_part[(row0[k] + s * rstride) * 2]);
-      mx = wave_max(mx);
-      const float mref = mx == -INFINITY ? 0.f : mx;
-      float L = l < ns[k] ? fast_exp2(ml[k][0] - mref) * ml[k][1] : 0.f;
-      for (int s = l + 64; s < ns[k]; s += 64) {
-        const f32x2 q = *reinterpret_cast<const f32x2*>(a.ml_part + (row0[k] + s * rstride) * 2);
-        L += fast_exp2(q[0] - mref) * q[1];
-      }
-      L = wave_sum(L);
-      const float inv_l = L > 0.f ? 1.f / L : 0.f;
-      if (kh == 0 && a.lse && l == 0) a.lse[static_cast<int64_t>(m0 + r) * a.h + i] = L > 0.f ? (mx + __log2f(L)) * kLn2 : -INFINITY;
-      // ---- merge: o = Σ_s 2^(m_s - M) / L · O_s over this lane's 4 columns
-      const float wl = l < ns[k] ? fast_exp2(ml[k][0] - mref) * inv_l : 0.f;  // weight of range l
-      f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) o += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u)) * v[k][u];
-      const float* src = a.o_part + row0[k] * 512 + kHalf * kh + 4 * l;
-      for (int s0 = kBatch; s0 < ns[k]; s0 += kBatch) {  // uniform: rows with more than 8 ranges
-        f32x4 q[kBatch];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u)
-          q[u] = s0 + u < ns[k] ? *reinterpret_cast<const f32x4*>(src + (s0 + u) * rstride * 512) : f32x4{0.f, 0.f, 0.f, 0.f};
-        float wb = 0.f;  // lane u < kBatch: weight of range s0 + u past the first 64
-        if (s0 >= 64 && l < kBatch && s0 + l < ns[k])
-          wb = fast_exp2(a.ml_part[(row0[k] + (s0 + l) * rstride) * 2] - mref) * inv_l;
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const float wu = s0 < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), s0 + u))
-                                   : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wb), u));
-          o += wu * q[u];
-        }
-      }
-      if (a.o_lat) {  // latent mode: the merged latent half row is the output
-        *reinterpret_cast<f32x4*>(a.o_lat + (static_cast<int64_t>(m0 + r) * a.h + i) * 512 + kHalf * kh + 4 * l) = o;
-        continue;
-      }
-      // o_lat as a hi + lo pair of bf16 (hi = bf16(o), lo = bf16(o - hi))
-      hv = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-      lv = u32x2{pack_bf16x2(o[0] - __uint_as_float(hv[0] << 16), o[1] - __uint_as_float(hv[0] & 0xFFFF0000u)),
-                 pack_bf16x2(o[2] - __uint_as_float(hv[1] << 16), o[3] - __uint_as_float(hv[1] & 0xFFFF0000u))};
+  for (int k = 0; k < RPW; ++k) {
+    const int r = rr[k];
+    if (r >= rows) continue;  // uniform
+    // ---- statistics over the ranges (ranges past 64 in a loop)
+    float mx = ml[k][0];
+    for (int s = l + 64; s < ns[k]; s += 64) mx = fmaxf(mx, a.ml_part[(row0[k] + s * rstride) * 2]);
+    mx = wave_max(mx);
+    const float mref = mx == -INFINITY ? 0.f : mx;
+    float L = l < ns[k] ? fast_exp2(ml[k][0] - mref) * ml[k][1] : 0.f;
+    for (int s = l + 64; s < ns[k]; s += 64) {
+      const f32x2 q = *reinterpret_cast<const f32x2*>(a.ml_part + (row0[k] + s * rstride) * 2);
+      L += fast_exp2(q[0] - mref) * q[1];
     }
-    // rows past `rows` stay zero: the MFMA below reads 32 rows
-    *(lds_u32x2*)(lds_ptr(s_hi) + r * kAStride + l * 8) = hv;
-    *(lds_u32x2*)(lds_ptr(s_lo) + r * kAStride + l * 8) = lv;
+    L = wave_sum(L);
+    const float inv_l = L > 0.f ? 1.f / L : 0.f;
+    if (a.lse && sub == 0 && l == 0) a.lse[static_cast<int64_t>(m0 + r) * a.h + i] = L > 0.f ? (mx + __log2f(L)) * kLn2 : -INFINITY;
+    // ---- merge: o = Σ_s 2^(m_s - M) / L · O_s over this lane's VW columns
+    const float wl = l < ns[k] ? fast_exp2(ml[k][0] - mref) * inv_l : 0.f;  // weight of range l
+    V o = V{};
+#pragma unroll
+    for (int u = 0; u < NB; ++u) o += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u)) * v[k][u];
+    const float* src = a.o_part + row0[k] * 512 + col0;
+    for (int s0 = NB; s0 < ns[k]; s0 += NB) {  // uniform: rows with more than NB ranges
+      V q[NB];
+#pragma unroll
+      for (int u = 0; u < NB; ++u) q[u] = s0 + u < ns[k] ? *reinterpret_cast<const V*>(src + (s0 + u) * rstride * 512) : V{};
+      float wb = 0.f;  // lane u < NB: weight of range s0 + u past the first 64
+      if (s0 >= 64 && l < NB && s0 + l < ns[k]) wb = fast_exp2(a.ml_part[(row0[k] + (s0 + l) * rstride) * 2] - mref) * inv_l;
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const float wu = s0 < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), s0 + u))
+                                 : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wb), u));
+        o += wu * q[u];
+      }
+    }
+    if (latent) {  // the merged latent row is the output
+      *reinterpret_cast<V*>(a.o_lat + (static_cast<int64_t>(m0 + r) * a.h + i) * 512 + col0) = o;
+      continue;
+    }
+    // o as a hi + lo pair of bf16 (hi = bf16(o), lo = bf16(o - hi)) into the MFMA rows
+    float x[VW];
+    __builtin_memcpy(x, &o, sizeof(x));
+    uint32_t hi[(VW + 1) / 2], lo[(VW + 1) / 2];
+    to_bf16_pair<VW>(x, hi, lo);
+    const int boff = r * kAStride + col0 * 2;
+    if constexpr (VW == 8) {
+      *(lds_u32x4*)(lds_ptr(s_hi) + boff) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+      *(lds_u32x4*)(lds_ptr(s_lo) + boff) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    } else if constexpr (VW == 4) {
+      *(lds_u32x2*)(lds_ptr(s_hi) + boff) = u32x2{hi[0], hi[1]};
+      *(lds_u32x2*)(lds_ptr(s_lo) + boff) = u32x2{lo[0], lo[1]};
+    } else if constexpr (VW == 2) {
+      *(__attribute__((address_space(3))) uint32_t*)(lds_ptr(s_hi) + boff) = hi[0];
+      *(__attribute__((address_space(3))) uint32_t*)(lds_ptr(s_lo) + boff) = lo[0];
+    } else {
+      *(__attribute__((address_space(3))) uint16_t*)(lds_ptr(s_hi) + boff) = static_cast<uint16_t>(hi[0]);
+      *(__attribute__((address_space(3))) uint16_t*)(lds_ptr(s_lo) + boff) = static_cast<uint16_t>(lo[0]);
+    }
   }
-  if (a.o_lat) return;  // uniform: no up-projection in latent mode
+  if (latent) return;  // uniform: no up-projection in latent mode
   __syncthreads();
-  if (w >= 4) return;
 
-  // ---- out[m][i*128 + 32w + ..] += (o_hi + o_lo)[m][half kh] · W_UV_i[half kh][32w + ..]
+  // ---- (o_hi + o_lo)[rows][half kh] · W_UV_i[half kh][32 cb + ..]; A row l%32 (zero
+  //      past the workgroup's rows), k = 16 ks + 8 (l/32) + e
   f32x16 acc = {};
-  const int arow = (l & 31) * kAStride + (l >> 5) * 16;
+  const int ar = l & 31;
+  const bool arow = ar < rows;
+  const int aoff = ar * kAStride + (l >> 5) * 16 + kh * 512;
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks) {
-    const u32x4 ah = *(lds_u32x4*)(lds_ptr(s_hi) + arow + ks * 32);
-    const u32x4 al = *(lds_u32x4*)(lds_ptr(s_lo) + arow + ks * 32);
+    u32x4 ah = {0u, 0u, 0u, 0u}, al = {0u, 0u, 0u, 0u};
+    if (arow) {
+      ah = *(lds_u32x4*)(lds_ptr(s_hi) + aoff + ks * 32);
+      al = *(lds_u32x4*)(lds_ptr(s_lo) + aoff + ks * 32);
+    }
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ah), as_bf16x8(bfr[ks]), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(al), as_bf16x8(bfr[ks]), acc, 0, 0, 0);
   }
-  const int width = a.h * 128;
-  const int col = i * 128 + 32 * w + (l & 31);
+  // rows 0 .. 15 of the 32x32 block are values 0 .. 7: row 8 (v / 4) + 4 (l / 32) + v % 4
+  if (kh == 1) {
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int r = 8 * (v / 4) + 4 * (l >> 5) + (v & 3);
+    for (int v8 = 0; v8 < 8; ++v8) s_x[cb][v8][l] = acc[v8];
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  const int width = a.h * 128;
+  const int col = i * 128 + 32 * cb + (l & 31);
+#pragma unroll
+  for (int v8 = 0; v8 < 8; ++v8) {
+    const int r = 8 * (v8 / 4) + 4 * (l >> 5) + (v8 & 3);
     if (r >= rows) continue;
     const int m = m0 + r;
-    float ov = acc[v];
-    if (a.gate) {  // out = sigmoid(g) (o_0 + o_1): each half carries its factor
+    float ov = acc[v8] + s_x[cb][v8][l];
+    if (a.gate) {  // out = sigmoid(g) o
       float g = 0.f;
       for (int ks = 0; ks < kGateSplit; ++ks) g += a.gate[(static_cast<int64_t>(ks) * M + m) * width + col];
       ov *= 1.f / (1.f + __expf(-g));
     }
-    atomicAdd(a.out + static_cast<int64_t>(m) * width + col, ov);
+    a.out[static_cast<int64_t>(m) * width + col] = ov;
   }
 }
 
 hipError_t launch_combine_bf16(const CombineArgs& a, hipStream_t s) {
   const int M = a.batch * a.n_q;
-  if (a.rows_per_wg < 1 || a.rows_per_wg > kWaves * kRowsPerWave || M <= 0) return hipErrorInvalidValue;
-  const dim3 grid(a.h, 2, (M + a.rows_per_wg - 1) / a.rows_per_wg);
-  combine_kernel<<<grid, kWaves * 64, 0, s>>>(a);
+  const int R = a.rows_per_wg;
+  if (!(R == 16 || R == 8 || R == 4 || R == 2 || R == 1) || M <= 0) return hipErrorInvalidValue;
+  const dim3 grid(a.h, (M + R - 1) / R);
+  if (R >= 8) combine_kernel<1><<<grid, kWaves * 64, 0, s>>>(a);
+  else if (R == 4) combine_kernel<2><<<grid, kWaves * 64, 0, s>>>(a);
+  else if (R == 2) combine_kernel<4><<<grid, kWaves * 64, 0, s>>>(a);
+  else combine_kernel<8><<<grid, kWaves * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -190,6 +190,52 @@ __device__ __forceinline__ void dma_b128(const u32x4& rsrc, uint32_t lane_off, u
       : "s"(lds), "v"(lane_off), "s"(off), "s"(rsrc)
       : "m0");
 }
+// A run of N (1, 2 or 4) such loads into consecutive 1 KiB blocks of LDS with one M0
+// write: load k lands at lds + 1024 k + 16 l and reads buffer offset
+// adj[k] + s + 1024 k. The instruction offset 1024 k moves the LDS and the buffer
+// address together; callers fold -1024 k into adj[k] (which must stay
+// non-negative), so the size bound still sees each load's true offset.
+template <int N>
+__device__ __forceinline__ void dma_run(const u32x4& rsrc, const uint32_t* adj, uint32_t s, uint32_t lds) {
+  static_assert(N == 1 || N == 2 || N == 4, "run length");
+  asm volatile("" : "+s"(s), "+s"(lds));  // registers, never folded literals
+  if constexpr (N == 1) {
+    uint32_t v0;
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "v_add_u32 %0, %2, %3\n\t"
+        "buffer_load_dwordx4 %0, %4, 0 offen lds"
+        : "=&v"(v0)
+        : "s"(lds), "v"(adj[0]), "s"(s), "s"(rsrc)
+        : "m0");
+  } else if constexpr (N == 2) {
+    uint32_t v0, v1;
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "v_add_u32 %0, %3, %5\n\t"
+        "v_add_u32 %1, %4, %5\n\t"
+        "buffer_load_dwordx4 %0, %6, 0 offen lds\n\t"
+        "buffer_load_dwordx4 %1, %6, 0 offen offset:1024 lds"
+        : "=&v"(v0), "=&v"(v1)
+        : "s"(lds), "v"(adj[0]), "v"(adj[1]), "s"(s), "s"(rsrc)
+        : "m0");
+  } else {
+    uint32_t v0, v1, v2, v3;
+    asm volatile(
+        "s_mov_b32 m0, %4\n\t"
+        "v_add_u32 %0, %5, %9\n\t"
+        "v_add_u32 %1, %6, %9\n\t"
+        "v_add_u32 %2, %7, %9\n\t"
+        "v_add_u32 %3, %8, %9\n\t"
+        "buffer_load_dwordx4 %0, %10, 0 offen lds\n\t"
+        "buffer_load_dwordx4 %1, %10, 0 offen offset:1024 lds\n\t"
+        "buffer_load_dwordx4 %2, %10, 0 offen offset:2048 lds\n\t"
+        "buffer_load_dwordx4 %3, %10, 0 offen offset:3072 lds"
+        : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
+        : "s"(lds), "v"(adj[0]), "v"(adj[1]), "v"(adj[2]), "v"(adj[3]), "s"(s), "s"(rsrc)
+        : "m0");
+  }
+}
 __device__ __forceinline__ void dma_b32(const u32x4& rsrc, uint32_t lane_off, uint32_t lds) {
   asm volatile("" : "+s"(lds));
   asm volatile(

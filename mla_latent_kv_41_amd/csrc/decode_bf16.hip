@@ -162,15 +162,17 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const int head_own = 32 * (qb_own - j_own * HB) + (l & 31);
   const int vis_own = kv - a.n_q + j_own;  // last visible position of this row
 
-  // ---- tile loads: wave load n' = n*NW + w fills LDS [n'*1024, +1024) = column
-  //      group G = n'/4, rows 8(n'%4) + l/8, chunk position l%8. Its source is
-  //      row t = 8(n'%4) + l/8, logical chunk 8G + ((l%8) ^ swz(t)); swz(t) only
-  //      depends on n'%2 and l, so the per-lane part of the offset takes two values.
-  uint32_t ld_lane[2];
+  // ---- tile loads: LDS block n = 4G + q (1 KiB) holds column group G, rows 8q + l/8,
+  //      chunk position l%8; its source is row t = 8q + l/8, logical chunk
+  //      8G + ((l%8) ^ swz(t)). Wave w loads groups w and w + 4 whole (runs of four
+  //      blocks, one M0 write each) and, with the RoPE key, block q = w of group 8.
+  //      ld_adj[q] is the per-lane offset of quarter q, less the 1024 q that the
+  //      run's instruction offset adds.
+  uint32_t ld_adj[4];
 #pragma unroll
-  for (int odd = 0; odd < 2; ++odd) {
-    const int t = 8 * odd + (l >> 3);
-    ld_lane[odd] = static_cast<uint32_t>(t * C::ROWB + (((l & 7) ^ swz(t)) << 4));
+  for (int q = 0; q < 4; ++q) {
+    const int t = 8 * q + (l >> 3);
+    ld_adj[q] = static_cast<uint32_t>(t * C::ROWB + (((l & 7) ^ swz(t)) << 4) - 1024 * q);
   }
 
   const char* cache = static_cast<const char*>(a.cache.data);
@@ -206,20 +208,20 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     return u32x4{static_cast<uint32_t>(ba), static_cast<uint32_t>(ba >> 32) & 0xFFFFu,
                  rows * static_cast<uint32_t>(C::ROWB), 0x00020000u};
   };
-  // Load n of this wave's share of a tile: wave load n' = n*NW + w fills LDS
-  // [n'*1024, +1024) from column group n'/4, rows 8(n'%4) .. +7; the whole byte
-  // offset is per lane (soffset 0) so the size bound applies to all of it.
-  auto issue_load = [&](const u32x4& rsrc, char* tile, int n) __attribute__((always_inline)) {
-    const int np = n * NW + w;  // wave-uniform
-    const int G = np >> 2, rq = np & 3;
-    dma_b128(rsrc, ld_lane[rq & 1], static_cast<uint32_t>(G * 128 + (rq >> 1) * 16 * C::ROWB),
-             static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_ptr(tile) + np * 1024)));
-  };
-  auto issue_tile = [&](int it, char* tile) __attribute__((always_inline)) {
-    const u32x4 rsrc = tile_rsrc(it);
+  // This wave's share of a tile (C::LOADS blocks). The whole byte offset is per lane
+  // (soffset 0), so the size bound applies to all of it.
+  static_assert(NW == 4 && C::LOADS == 8 + (DR == 64 ? 1 : 0), "load runs");
+  auto issue_loads = [&](const u32x4& rsrc, char* tile) __attribute__((always_inline)) {
+    const uint32_t base = lds_addr(tile);
 #pragma unroll
-    for (int n = 0; n < C::LOADS; ++n) issue_load(rsrc, tile, n);
+    for (int r = 0; r < 2; ++r) {
+      const int G = w + 4 * r;
+      dma_run<4>(rsrc, ld_adj, static_cast<uint32_t>(G * 128), base + G * 4096);
+    }
+    if constexpr (DR == 64)
+      dma_run<1>(rsrc, ld_adj + w, static_cast<uint32_t>(8 * 128 + 1024 * w), base + 8 * 4096 + 1024 * w);
   };
+  auto issue_tile = [&](int it, char* tile) __attribute__((always_inline)) { issue_loads(tile_rsrc(it), tile); };
 
   // ---- per-lane LDS read offsets
   // score A operand: row t = l%32, logical chunk k = 2ks + l/32: group ks/4,
@@ -412,12 +414,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     // tile i + 2 into the buffer of tile i - 2, as one burst ahead of the score
     // chain: measured cheaper than loads spread through the MFMAs, and far cheaper
     // than loads among the value phase's transposed LDS reads
-    if (i + 2 < n_tiles) {
-      char* nxt = tile_ptr(Ic<(K + 2) % 4>{});
-      const u32x4 rs = tile_rsrc(i + 2);
-#pragma unroll
-      for (int n = 0; n < C::LOADS; ++n) issue_load(rs, nxt, n);
-    }
+    if (i + 2 < n_tiles) issue_tile(i + 2, tile_ptr(Ic<(K + 2) % 4>{}));
     f32x16 sc = scores(tile_ptr(kc), [](int) {});
     if (i >= first_masked) apply_mask(sc, i);  // uniform
     SoftState st;
@@ -590,13 +587,14 @@ __global__ __launch_bounds__(256) void decode_roles_kernel(DecodeArgs a) {
   const int head_own = 32 * (qb_own - j_own * HB) + (l & 31);
   const int vis_own = kv - a.n_q + j_own;
 
-  // ---- tile loads (value waves): wave load n' = 2n + v fills LDS [n'*1024, +1024) =
-  //      column group n'/4, rows 8(n'%4) + l/8, chunk position l%8
-  uint32_t ld_lane[2];
+  // ---- tile loads (value waves), in the LDS block layout of the 128-row form: value
+  //      wave v loads groups v, v + 2, v + 4, v + 6 whole (runs of four blocks) and,
+  //      with the RoPE key, blocks 2v and 2v + 1 of group 8 (a run of two)
+  uint32_t ld_adj[4];
 #pragma unroll
-  for (int odd = 0; odd < 2; ++odd) {
-    const int t = 8 * odd + (l >> 3);
-    ld_lane[odd] = static_cast<uint32_t>(t * ROWB + (((l & 7) ^ swz(t)) << 4));
+  for (int q = 0; q < 4; ++q) {
+    const int t = 8 * q + (l >> 3);
+    ld_adj[q] = static_cast<uint32_t>(t * ROWB + (((l & 7) ^ swz(t)) << 4) - 1024 * q);
   }
   const char* cache = static_cast<const char*>(a.cache.data);
   const bool paged = a.cache.block_table != nullptr;
@@ -666,15 +664,17 @@ __global__ __launch_bounds__(256) void decode_roles_kernel(DecodeArgs a) {
       return u32x4{static_cast<uint32_t>(ba), static_cast<uint32_t>(ba >> 32) & 0xFFFFu,
                    rows * static_cast<uint32_t>(ROWB), 0x00020000u};
     };
+    static_assert(LOADS == 16 + (DR == 64 ? 2 : 0), "load runs");
     auto issue_tile = [&](int it, char* tile) __attribute__((always_inline)) {
       const u32x4 rsrc = tile_rsrc(it);
+      const uint32_t base = lds_addr(tile);
 #pragma unroll
-      for (int n = 0; n < LOADS; ++n) {
-        const int np = 2 * n + vw;  // wave-uniform
-        const int G = np >> 2, rq = np & 3;
-        dma_b128(rsrc, ld_lane[rq & 1], static_cast<uint32_t>(G * 128 + (rq >> 1) * 16 * ROWB),
-                 static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_ptr(tile) + np * 1024)));
+      for (int r = 0; r < 4; ++r) {
+        const int G = vw + 2 * r;
+        dma_run<4>(rsrc, ld_adj, static_cast<uint32_t>(G * 128), base + G * 4096);
       }
+      if constexpr (DR == 64)
+        dma_run<2>(rsrc, ld_adj + 2 * vw, static_cast<uint32_t>(8 * 128 + 2048 * vw), base + 8 * 4096 + 2048 * vw);
     };
     constexpr int SDEPTH = 6;
     auto scores = [&](const char* tile) __attribute__((always_inline)) {

@@ -56,7 +56,6 @@ struct QPrepArgs {
   uint16_t* q_lo;           // same order: bf16 of what q_cat's rounding left, or nullptr
   const float* q_abs;       // latent mode: the absorbed query [M][h][512] fp32 given (no W_UK product), or nullptr
   int32_t M, n_q, h, d_r, max_kv_len;
-  float* out;               // [M][h*128] output, zeroed for the combine's atomic adds (nullptr: not zeroed)
   float qscale;             // scale * log2(e)
   double inv_freq[32];      // rope_base^(-2k/d_r), computed on the host in fp64
   PlanArgs plan;
@@ -90,11 +89,11 @@ struct CombineArgs {
   const int32_t* seq_off;   // [batch + 1] first partial index of each sequence
   const uint16_t* w_uv_pk;  // packed W_UV
   const float* gate;        // [16][M][h*128] pre-activation gate logit splits, or nullptr
-  float* out;               // [M][h*128], zeroed beforehand: halves are added atomically
+  float* out;               // [M][h*128]: one plain store per element
   float* o_lat;             // latent mode: [M][h][512] merged latent output (no W_UV), or nullptr
   float* lse;               // [M][h] or nullptr
   int32_t batch, n_q, h;
-  int32_t rows_per_wg;      // query rows per workgroup, 1..32
+  int32_t rows_per_wg;      // query rows per workgroup: 16, 8, 4, 2 or 1
 };
 hipError_t launch_combine_bf16(const CombineArgs& a, hipStream_t s);
 

@@ -128,8 +128,8 @@ __device__ void build_plan(const PlanArgs& p, int l) {
 // of the 4 heads at one (row, column chunk) are adjacent lanes of the block order
 // above; the 4 waves' pieces of a line meet in the L2 of this workgroup's XCD.
 //
-// Waves 4-7 (side work, concurrent with the product's loads): zero the output rows
-// m = nb (mod 8) of these heads and rotate their q_R. The rotation angle depends on
+// Waves 4-7 (side work, concurrent with the product's loads): rotate the q_R of
+// query rows m = nb (mod 8) of these heads. The rotation angle depends on
 // the row and the pair only: each half wave takes one row, lane k forms the sine and
 // cosine of pair k once, and the 4 heads' chunks fetch them by lane shuffles. Wave 4
 // of workgroup (0, 0) first builds the split plan.
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(512) void qprep_kernel(QPrepArgs a) {
 
   if (w >= kQHeads) {
     // ================= side work: waves 4-7 =================
-    const int sw = w - kQHeads, st = tid - 64 * kQHeads;
+    const int sw = w - kQHeads;
     if (g == 0 && nb == 0 && sw == 0) build_plan(a.plan, l);
     const int srows = a.M > nb ? (a.M - nb + kQColBlocks - 1) / kQColBlocks : 0;
     // RoPE of q_R: half wave hf of wave sw takes side row t = 8u + 2sw + hf (u = 0, 1, ..),
@@ -199,12 +199,6 @@ __global__ __launch_bounds__(512) void qprep_kernel(QPrepArgs a) {
         *reinterpret_cast<u32x4*>(a.q_cat + off) = o;
         if (lo_out) *reinterpret_cast<u32x4*>(a.q_lo + off) = ol;
       }
-    }
-    // zero the output rows m = nb (mod 8) of these heads (the combine adds into them)
-    const int per_row = nh * 32;  // float4 per row of this head group
-    for (int idx = st; a.out && idx < srows * per_row; idx += 64 * kQHeads) {
-      const int m = nb + kQColBlocks * (idx / per_row), q = idx % per_row;
-      *reinterpret_cast<f32x4*>(a.out + (static_cast<int64_t>(m) * a.h + i0) * 128 + 4 * q) = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     return;
   }

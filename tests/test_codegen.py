@@ -58,13 +58,22 @@ def test_device_code_properties(name):
         assert not SCALAR_WRITE.match(mnem), s
         assert not PACKED_F32.match(mnem), s
         if re.search(r"\bm0\b", s):
-            # only writes of M0 from an SGPR, each followed by a direct-to-LDS load
+            # only writes of M0 from an SGPR, each followed, after at least one address
+            # add (the wait state M0 needs) and nothing else, by a direct-to-LDS load
             assert re.match(r"^s_mov_b32 m0, s\d+$", s), s
-            nxt = [t for t in insts[k + 1:k + 4] if t.startswith("buffer_load")]
-            assert nxt and nxt[0].endswith(" lds"), (s, insts[k + 1:k + 4])
+            j = k + 1
+            while j < len(insts) and insts[j].startswith("v_add_u32"):
+                j += 1
+            assert j > k + 1 and j < len(insts) and insts[j].startswith("buffer_load") and \
+                insts[j].endswith(" lds"), (s, insts[k + 1:j + 1])
         if mnem.startswith("buffer_load") and s.endswith(" lds"):
-            prev = [t for t in insts[max(0, k - 3):k] if "m0" in t]
-            assert prev, ("direct-to-LDS load without its M0 write", s)
+            # a run of direct-to-LDS loads and their address adds goes back to its M0 write
+            j = k - 1
+            while j >= 0 and (insts[j].startswith("v_add_u32") or
+                              (insts[j].startswith("buffer_load") and insts[j].endswith(" lds"))):
+                j -= 1
+            assert j >= 0 and re.match(r"^s_mov_b32 m0, s\d+$", insts[j]), \
+                ("direct-to-LDS load without its M0 write", s)
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipcc") is None, reason="hipcc not found")
