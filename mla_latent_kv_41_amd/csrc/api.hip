@@ -67,7 +67,8 @@ size_t elem_bytes(int dtype) { return dtype == MLA_F32 ? 4 : 2; }
 // not, and a short sequence costs little either way.
 constexpr int kPreciseBelow = 4096;
 constexpr int kMaxSplitsPerSeq = 1024;  // bound on a sequence's token ranges
-constexpr int kMinRaggedChunk = 256;    // tokens per range at least, ragged batches
+constexpr int kMinRaggedChunk = 256;   // tokens per range at least, ragged batches
+constexpr int kRaggedPerSlot = 2;      // ragged batches: workgroups per CU slot
 constexpr int kRowsRangeMin = 1024;     // see the fast form's choice below
 
 struct Plan {
@@ -121,13 +122,12 @@ Plan plan_bf16(const Resolved& r, const mla_decode_args* a) {
   if (a->num_splits > 0) {
     chunk = ceil_div(L, a->num_splits);
   } else if (ragged) {
-    // ranges sized so the batch yields about three workgroups per slot (measured on
-    // the ragged two-query workload: 1, 2, 3, 4 per slot give an attention kernel of
-    // 370, 332, 323, 335 us; more ranges balance the lengths better until the
-    // combine's extra partial rows outweigh it)
-    // (at least kMinRaggedChunk tokens, so the fp32 partials of a range stay well
-    // below the bytes of cache it reads)
-    chunk = std::max<int64_t>(kMinRaggedChunk, ceil_div(total_units, 3 * target));
+    // ranges sized so the batch yields about two workgroups per slot: more ranges
+    // balance the lengths better, but every range writes fp32 partial rows that the
+    // combine reads back (measured on the ragged two-query workload, step 407 us at
+    // two per slot against 447 at three and 471 at four), at least kMinRaggedChunk
+    // tokens, so the partials of a range stay well below the cache bytes it reads
+    chunk = std::max<int64_t>(kMinRaggedChunk, ceil_div(total_units, kRaggedPerSlot * target));
   } else {
     // one workgroup per slot when every sequence is as long as the longest
     const int64_t units = static_cast<int64_t>(a->batch) * groups_of(L);
@@ -190,10 +190,12 @@ Workspace layout_ws(const Resolved& r, const mla_decode_args* a, const Plan* p) 
     off = align_up(off + 2 * sizeof(int32_t));
     w.seq_off = off;
     off = align_up(off + (static_cast<size_t>(a->batch) + 1) * sizeof(int32_t));
-    w.fast_list = off;  // both lists always exist: the device plan may fill either
-    off = align_up(off + cap * sizeof(WorkItem));
+    // both lists always exist (the device plan may fill either), each with kListPad
+    // entries past cap: a launch's grid, padded to 8 workgroups, reads up to there
+    w.fast_list = off;
+    off = align_up(off + (cap + kListPad) * sizeof(WorkItem));
     w.prec_list = off;
-    off = align_up(off + cap * sizeof(WorkItem));
+    off = align_up(off + (cap + kListPad) * sizeof(WorkItem));
     w.q_cat = off;
     off = align_up(off + M * r.h * row * 2);
     if (p->prec_pairs > 0) {
@@ -367,7 +369,6 @@ mla_status decode_impl(const mla_dims* dims, const CacheRef& cache, const mla_de
   const bool two = fast_units > 0 && prec_units > 0;
   if (fast_units > 0) {
     d.list = fast_list;
-    d.count = counts;
     d.form = p.fast_form;
     d.units = static_cast<int32_t>(fast_units);
     if (launch_decode_bf16(d, stream, a->ev_attn_begin, two ? nullptr : a->ev_attn_end) != hipSuccess)
@@ -375,7 +376,6 @@ mla_status decode_impl(const mla_dims* dims, const CacheRef& cache, const mla_de
   }
   if (prec_units > 0) {
     d.list = prec_list;
-    d.count = counts + 1;
     d.chunk = p.chunk_precise;
     d.form = kFormPrecise;
     d.units = static_cast<int32_t>(prec_units);

@@ -147,8 +147,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   int u = blockIdx.x;
   if ((a.units & 7) == 0) u = (blockIdx.x & 7) * (a.units >> 3) + (blockIdx.x >> 3);
   const int pair = u / hgroups, hg = u - pair * hgroups;
-  if (pair >= *a.count) return;  // uniform: past the pairs of this launch
   const WorkItem item = a.list[pair];
+  if (item.b < 0) return;  // uniform: past the pairs of this launch
   const int b = item.b, kv = item.kv;
   const int t_begin = item.s * a.chunk;
   const int t_end = min(t_begin + a.chunk, kv);
@@ -572,8 +572,8 @@ __global__ __launch_bounds__(256) void decode_roles_kernel(DecodeArgs a) {
   int u = blockIdx.x;
   if ((a.units & 7) == 0) u = (blockIdx.x & 7) * (a.units >> 3) + (blockIdx.x >> 3);
   const int pair = u / hgroups, hg = u - pair * hgroups;
-  if (pair >= *a.count) return;  // uniform: past the pairs of this launch
   const WorkItem item = a.list[pair];
+  if (item.b < 0) return;  // uniform: past the pairs of this launch
   const int b = item.b, kv = item.kv;
   const int t_begin = item.s * a.chunk;
   const int t_end = min(t_begin + a.chunk, kv);

@@ -43,9 +43,10 @@ struct PlanArgs {
   int32_t batch, n_q, max_kv_len, chunk_fast, chunk_precise, precise_below, cap;
   int32_t* counts;    // [0] pairs in the fast list, [1] in the precise list
   int32_t* seq_off;   // [batch + 1]
-  WorkItem* fast;     // [cap]
-  WorkItem* precise;  // [cap]
+  WorkItem* fast;     // [cap + kListPad]: the pairs, then entries with b = -1
+  WorkItem* precise;  // [cap + kListPad]
 };
+constexpr int kListPad = 8;  // list entries past cap (grids are padded to 8 workgroups)
 
 struct QPrepArgs {
   const uint16_t* q_nope;   // [M][h][128]
@@ -73,8 +74,7 @@ struct DecodeArgs {
   CacheRef cache;
   const uint16_t* q_cat;   // block order (written by qprep_kernel)
   const uint16_t* q_lo;    // kFormPrecise: the low halves, same order
-  const WorkItem* list;    // the pairs this launch takes
-  const int32_t* count;    // number of pairs in `list` (device)
+  const WorkItem* list;    // the pairs this launch takes, then entries with b = -1
   float* o_part;           // [pairs][n_q][h][512] fp32, O relative to the row's reference m
   float* ml_part;          // [pairs][n_q][h][2] (m, l), base-2 units
   int32_t n_q, h, d_r, chunk;

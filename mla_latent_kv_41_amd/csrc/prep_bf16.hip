@@ -113,6 +113,11 @@ __device__ void build_plan(const PlanArgs& p, int l) {
     p.counts[0] = min(of, p.cap);
     p.counts[1] = min(op, p.cap);
   }
+  // the rest of both lists, up to cap + kListPad, holds b = -1: a workgroup reads its
+  // pair's entry and stops there, without waiting for the counts first
+  const int nf_all = __shfl(of, 63), np_all = __shfl(op, 63);
+  for (int k = nf_all + l; k < p.cap + kListPad; k += 64) p.fast[k] = WorkItem{-1, 0, 0, 0};
+  for (int k = np_all + l; k < p.cap + kListPad; k += 64) p.precise[k] = WorkItem{-1, 0, 0, 0};
 }
 
 // grid (ceil(h / 4), 8), 8 waves: group g of 4 heads (4g .. 4g + 3), block nb of 64

@@ -84,7 +84,7 @@ def expected_workspace(*, h, n_q, batch, L, d_rope=64, host=None, num_splits=0, 
     if num_splits:
         chunk = cdiv(L, num_splits)
     elif ragged:
-        chunk = max(256, cdiv(units, 3 * 256))
+        chunk = max(256, cdiv(units, 2 * 256))
     else:
         chunk = cdiv(L, min(cdiv(256, batch * groups(L)), cdiv(L, 32)))
     chunk = max(chunk, cdiv(L, 1024))
@@ -104,7 +104,7 @@ def expected_workspace(*, h, n_q, batch, L, d_rope=64, host=None, num_splits=0, 
     al = lambda x: cdiv(x, ALIGN) * ALIGN
     M = batch * n_q
     q = al(M * h * (512 + d_rope) * 2)
-    n = al(8) + al((batch + 1) * 4) + 2 * al(max(cap, 1) * 16) + q + (q if prec else 0)
+    n = al(8) + al((batch + 1) * 4) + 2 * al((max(cap, 1) + 8) * 16) + q + (q if prec else 0)
     n += al(max(cap, 1) * n_q * h * 512 * 4) + al(max(cap, 1) * n_q * h * 8)
     if gated:
         n += al(16 * M * h * 128 * 4)
