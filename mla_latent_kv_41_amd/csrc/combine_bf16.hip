@@ -64,10 +64,10 @@ __device__ __forceinline__ void to_bf16_pair(const float (&x)[N], uint32_t (&hi)
 // 32 output columns of block w % 4 over latent half w / 4 (its 16 W_UV_i fragments
 // are loaded first); waves 4-7 hand their sums to waves 0-3 through LDS, which add
 // them, apply the gate and store.
-template <int WPR>
+template <int WPR, int RPW>
 __global__ __launch_bounds__(kWaves * 64) void combine_kernel(CombineArgs a) {
   constexpr int VW = 8 / WPR;              // floats per lane of a row
-  constexpr int RPW = WPR == 1 ? 2 : 1;    // row slots per wave
+  static_assert(RPW == 1 || WPR == 1, "two rows per wave only with whole rows");
   constexpr int NB = WPR == 1 ? 4 : 8;     // partial rows per row in flight
   using V = typename VecT<VW>::T;
   __shared__ __attribute__((aligned(16))) char s_hi[kMaxRows * kAStride];
@@ -228,10 +228,11 @@ hipError_t launch_combine_bf16(const CombineArgs& a, hipStream_t s) {
   const int R = a.rows_per_wg;
   if (!(R == 16 || R == 8 || R == 4 || R == 2 || R == 1) || M <= 0) return hipErrorInvalidValue;
   const dim3 grid(a.h, (M + R - 1) / R);
-  if (R >= 8) combine_kernel<1><<<grid, kWaves * 64, 0, s>>>(a);
-  else if (R == 4) combine_kernel<2><<<grid, kWaves * 64, 0, s>>>(a);
-  else if (R == 2) combine_kernel<4><<<grid, kWaves * 64, 0, s>>>(a);
-  else combine_kernel<8><<<grid, kWaves * 64, 0, s>>>(a);
+  if (R == 16) combine_kernel<1, 2><<<grid, kWaves * 64, 0, s>>>(a);
+  else if (R == 8) combine_kernel<1, 1><<<grid, kWaves * 64, 0, s>>>(a);
+  else if (R == 4) combine_kernel<2, 1><<<grid, kWaves * 64, 0, s>>>(a);
+  else if (R == 2) combine_kernel<4, 1><<<grid, kWaves * 64, 0, s>>>(a);
+  else combine_kernel<8, 1><<<grid, kWaves * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -810,14 +810,15 @@ __global__ __launch_bounds__(256) void decode_roles_kernel(DecodeArgs a) {
     if constexpr (SC) {
       const int64_t qoff = (static_cast<int64_t>(b) * a.n_q * HB + qb_own) * KS * 64 + l;
       const u32x4* qp = reinterpret_cast<const u32x4*>(a.q_cat) + qoff;
+      const u32x4* qlp = reinterpret_cast<const u32x4*>(PRECISE ? a.q_lo : a.q_cat) + qoff;
+      // No wait here: the compiler's own wait before each fragment's first use lets
+      // the first score chain start while the later fragments are still arriving.
+      // Score waves issue no other vector loads, so those waits cost nothing later.
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[ks] = qp[ks * 64];
-      if constexpr (PRECISE) {
-        const u32x4* qlp = reinterpret_cast<const u32x4*>(a.q_lo) + qoff;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) ql[ks] = qlp[ks * 64];
+      for (int ks = 0; ks < KS; ++ks) {
+        qf[ks] = qp[ks * 64];
+        if constexpr (PRECISE) ql[ks] = qlp[ks * 64];
       }
-      wait_vm<0>();
     }
     for (int pass = 0;; ++pass) {
       const bool allow_restart = pass < kMaxRestarts;
