@@ -314,6 +314,19 @@ def summarize_append_trace(d):
     print("fused append trace summary written")
 
 
+def _copy_calibration(vals):
+    """What FETCH_SIZE and WRITE_SIZE (KiB) count for the one 512 MiB device copy of a
+    counter run: the sum over its dispatches (the runtime may split the copy into
+    several dispatches of the same grid), checked against the bytes it writes."""
+    copy = [k for k in vals if "copyBuffer" in k[0] and k[1] == COPY_BYTES // 4096]
+    if len(copy) != 1:
+        raise SystemExit("calibration copy not found in the counter runs")
+    cf = {c: sum(v) for c, v in vals[copy[0]].items()}
+    if abs(cf["WRITE_SIZE"] * 1024 / COPY_BYTES - 1) > 0.05:
+        raise SystemExit("calibration copy dispatches write %.0f KiB, not 512 MiB" % cf["WRITE_SIZE"])
+    return cf
+
+
 def _counter_table(d, sub):
     """{(kernel, grid): {counter: [values]}} of the FETCH_SIZE and WRITE_SIZE runs
     under DIR/sub, and the calibration factors from the 512 MiB copy."""
@@ -326,10 +339,7 @@ def _counter_table(d, sub):
             for r in csv.DictReader(open(f)):
                 vals[(_short_kernel_name(r["Kernel_Name"]), int(r["Grid_Size"]))][r["Counter_Name"]].append(
                     float(r["Counter_Value"]))
-    copy = [k for k in vals if "copyBuffer" in k[0] and k[1] == COPY_BYTES // 4096]
-    if len(copy) != 1:
-        raise SystemExit("calibration copy not found in the counter runs under %s" % sub)
-    cf = {c: sum(v) / len(v) for c, v in vals[copy[0]].items()}
+    cf = _copy_calibration(vals)
     return vals, cf, COPY_BYTES / (cf["FETCH_SIZE"] * 1024), COPY_BYTES / (cf["WRITE_SIZE"] * 1024)
 
 
@@ -485,10 +495,7 @@ def summarize_traffic(d, cfg):
             for r in csv.DictReader(open(f)):
                 vals[(_short_kernel_name(r["Kernel_Name"]), int(r["Grid_Size"]))][r["Counter_Name"]].append(
                     float(r["Counter_Value"]))
-    copy = [k for k in vals if "copyBuffer" in k[0] and k[1] == COPY_BYTES // 4096]
-    if len(copy) != 1:
-        raise SystemExit("calibration copy not found in the counter runs")
-    cf = {c: sum(v) / len(v) for c, v in vals[copy[0]].items()}
+    cf = _copy_calibration(vals)
     f_fac = COPY_BYTES / (cf["FETCH_SIZE"] * 1024)
     w_fac = COPY_BYTES / (cf["WRITE_SIZE"] * 1024)
     attn = sorted(k for k in vals if k[0].startswith(ATTENTION_KERNELS))
@@ -513,8 +520,9 @@ def summarize_traffic(d, cfg):
         ws = cs.get("WRITE_SIZE", [float("nan")])
         lines.append("| `%s` | %d | %d | %.1f | %.1f |" % (n, g, len(fs), sum(fs) / len(fs), sum(ws) / len(ws)))
     alg = lines_of["FETCH_SIZE"]["roofline"]["algorithmic_bytes_per_launch"]
-    lines += ["", "Calibration: the 512 MiB copy reads and writes %d bytes; FETCH_SIZE counts %.1f KiB "
-              "(factor %.4f bytes per counted byte) and WRITE_SIZE %.1f KiB (factor %.4f)." % (
+    lines += ["", "Calibration: the 512 MiB copy reads and writes %d bytes; summed over its dispatches, "
+              "FETCH_SIZE counts %.1f KiB (factor %.4f bytes per counted byte) and WRITE_SIZE %.1f KiB "
+              "(factor %.4f)." % (
                   COPY_BYTES, cf["FETCH_SIZE"], f_fac, cf["WRITE_SIZE"], w_fac), "",
               "Attention launches of one step (%s): fetch %.1f MB, write %.1f MB, total %.1f MB, against %.1f MB "
               "algorithmic (%.2fx)." % (kname, fetch_b / 1e6, write_b / 1e6, (fetch_b + write_b) / 1e6, alg / 1e6,
