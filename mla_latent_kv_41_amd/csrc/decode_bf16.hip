@@ -95,6 +95,50 @@ struct Ic {
   static constexpr int value = V;
 };
 
+// Phase stamps (instrumented builds only, compiled with -DMLA_STAMPS): each wave of
+// a workgroup whose unit is below kStampUnits reads the shader clock (s_memtime) at
+// entry, right after every step's barrier (where the wave has no LDS operation
+// outstanding, so a read costs one scalar round trip and no other wait), after its
+// last value pass and after its epilogue's stores have completed, and writes
+//   [0] entry, [1] first step's barrier, [2] last step's barrier, [3] barriers
+//   passed, [4] sum of the intervals between consecutive barriers, [5] shortest,
+//   [6] longest, [7] after the last value pass, [8] stores complete
+// to stamp_buf[unit][wave][kStampSlots]. Product builds compile none of it.
+#ifdef MLA_STAMPS
+constexpr bool kStamps = true;
+#else
+constexpr bool kStamps = false;
+#endif
+constexpr int kStampUnits = 64, kStampSlots = 16;
+struct StampRec {
+  uint64_t v[9];
+  __device__ __forceinline__ void begin() {
+    v[0] = __builtin_amdgcn_s_memtime();
+    v[3] = v[4] = v[6] = 0;
+    v[5] = ~0ull;
+  }
+  __device__ __forceinline__ void step() {  // right after a barrier
+    const uint64_t t = __builtin_amdgcn_s_memtime();
+    if (v[3] == 0) {
+      v[1] = t;
+    } else {
+      const uint64_t d = t - v[2];
+      v[4] += d;
+      v[5] = d < v[5] ? d : v[5];
+      v[6] = d > v[6] ? d : v[6];
+    }
+    v[2] = t;
+    ++v[3];
+  }
+  __device__ __forceinline__ void loop_end() { v[7] = __builtin_amdgcn_s_memtime(); }
+  __device__ __forceinline__ void end(uint64_t* buf, int unit, int wave, int lane) {
+    wait_vm<0>();
+    v[8] = __builtin_amdgcn_s_memtime();
+    if (unit < kStampUnits && lane == 0)
+      for (int k = 0; k < 9; ++k) buf[(static_cast<int64_t>(unit) * 4 + wave) * kStampSlots + k] = v[k];
+  }
+};
+
 // Score MFMA in VGPR form: Sᵀ += A · B with the accumulator in VGPRs. (The
 // compiler selects the AGPR form for every builtin MFMA of this kernel, whose AGPRs
 // hold the value accumulators.) The leading s_nop gives the 2 wait states a VALU
@@ -146,6 +190,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   // range of units so one sequence's splits (and head groups) share an L2.
   int u = blockIdx.x;
   if ((a.units & 7) == 0) u = (blockIdx.x & 7) * (a.units >> 3) + (blockIdx.x >> 3);
+  StampRec stamp;
+  if constexpr (kStamps) stamp.begin();
   const int pair = u / hgroups, hg = u - pair * hgroups;
   const WorkItem item = a.list[pair];
   if (item.b < 0) return;  // uniform: past the pairs of this launch
@@ -411,6 +457,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     constexpr bool FIRST = decltype(first)::value != 0;
     wait_tiles(i + 1 < n_tiles ? 1 : 0);  // tile i has landed
     lds_barrier();  // tile i and P of tile i - 1 everywhere; tile i - 2 is free
+    if constexpr (kStamps) stamp.step();
     // tile i + 2 into the buffer of tile i - 2, as one burst ahead of the score
     // chain: measured cheaper than loads spread through the MFMAs, and far cheaper
     // than loads among the value phase's transposed LDS reads
@@ -486,6 +533,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       const int kl = (n_tiles - 1) & 3;
       const char* lt = kl == 0 ? s_tile0 : kl == 1 ? s_tile1 : kl == 2 ? s_tile2 : s_tile3;
       pv(lt, s_p + ((n_tiles - 1) & 1) * PBUF, [](int) {}, [](int) {}, Ic<0>{});
+      if constexpr (kStamps) stamp.loop_end();
       break;
     }
     // restart the range with the largest score seen as every row's reference; the
@@ -519,6 +567,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     ml[0] = m_ref;
     ml[1] = l_run;
   }
+  if constexpr (kStamps) stamp.end(a.stamps, u, w, l);
 }
 
 // Role-split form for 64 query rows per workgroup (a (sequence, token range, head
@@ -571,6 +620,8 @@ __global__ __launch_bounds__(256) void decode_roles_kernel(DecodeArgs a) {
   const int HB = a.h / 32;
   int u = blockIdx.x;
   if ((a.units & 7) == 0) u = (blockIdx.x & 7) * (a.units >> 3) + (blockIdx.x >> 3);
+  StampRec stamp;
+  if constexpr (kStamps) stamp.begin();
   const int pair = u / hgroups, hg = u - pair * hgroups;
   const WorkItem item = a.list[pair];
   if (item.b < 0) return;  // uniform: past the pairs of this launch
@@ -780,6 +831,7 @@ __global__ __launch_bounds__(256) void decode_roles_kernel(DecodeArgs a) {
         else wait_vm<0>();
       }
       lds_barrier();  // tile i and P of tile i - 1 everywhere; tile i - 2 is free
+      if constexpr (kStamps) stamp.step();
       if constexpr (!SC) {
         if (i + 2 < n_tiles) issue_tile(i + 2, tile_ptr(Ic<(K + 2) % 4>{}));
         if constexpr (!FIRST) pv(tile_ptr(Ic<(K + 3) % 4>{}), s_p + ((K + 1) & 1) * PBUF);
@@ -852,6 +904,7 @@ __global__ __launch_bounds__(256) void decode_roles_kernel(DecodeArgs a) {
           const char* lt = kl == 0 ? s_tile0 : kl == 1 ? s_tile1 : kl == 2 ? s_tile2 : s_tile3;
           pv(lt, s_p + ((n_tiles - 1) & 1) * PBUF);
         }
+        if constexpr (kStamps) stamp.loop_end();
         break;
       }
       if constexpr (!SC) wait_vm<0>();
@@ -887,9 +940,19 @@ __global__ __launch_bounds__(256) void decode_roles_kernel(DecodeArgs a) {
   };
   if (scorer) run(Ic<1>{});
   else run(Ic<0>{});
+  if constexpr (kStamps) stamp.end(a.stamps, u, w, l);
 }
 
-hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+#ifdef MLA_STAMPS
+__device__ uint64_t stamp_buf[kStampUnits * 4 * kStampSlots];
+#endif
+
+hipError_t launch_decode_bf16(const DecodeArgs& a_in, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+  DecodeArgs a = a_in;
+#ifdef MLA_STAMPS
+  if (hipGetSymbolAddress(reinterpret_cast<void**>(&a.stamps), HIP_SYMBOL(stamp_buf)) != hipSuccess)
+    return hipErrorInvalidSymbol;
+#endif
   // hipExtLaunchKernelGGL stamps ev0/ev1 from the dispatch itself, so an event pair
   // brackets exactly this kernel's execution (null events: plain launch).
   const int rows = a.h * a.n_q;
@@ -918,3 +981,13 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s, hipEvent_t ev0
 }
 
 }  // namespace mla
+
+#ifdef MLA_STAMPS
+// Instrumented builds only: the device address and size of the stamp buffer (see
+// StampRec). Returns 0, or -1 if the address cannot be looked up.
+extern "C" int32_t mla_stamps_buffer(void** ptr, size_t* bytes) {
+  if (!ptr || !bytes) return -1;
+  *bytes = sizeof(mla::stamp_buf);
+  return hipGetSymbolAddress(ptr, HIP_SYMBOL(mla::stamp_buf)) == hipSuccess ? 0 : -1;
+}
+#endif

@@ -80,6 +80,7 @@ struct DecodeArgs {
   int32_t n_q, h, d_r, chunk;
   int32_t form;            // DecodeForm
   int32_t units;           // workgroups launched: pairs the list may hold x head groups
+  uint64_t* stamps;        // instrumented builds: the phase stamp buffer (set by the launcher)
 };
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 

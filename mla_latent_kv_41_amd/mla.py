@@ -12,7 +12,9 @@ import os
 from typing import Optional, Sequence
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmla.so")
+# MLA_LIB_PATH selects another build of the same library (the phase-stamp tool's
+# instrumented build); by default the in-tree libmla.so
+LIB_PATH = os.environ.get("MLA_LIB_PATH") or os.path.join(HERE, "libmla.so")
 
 MLA_OK, MLA_E_NULL, MLA_E_SHAPE, MLA_E_DTYPE, MLA_E_UNSUPPORTED, MLA_E_WORKSPACE, MLA_E_HIP = range(7)
 MLA_F32, MLA_BF16 = 0, 1

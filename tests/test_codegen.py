@@ -21,9 +21,9 @@ HIPCC = build.HIPCC
 
 
 @functools.lru_cache(maxsize=None)
-def device_asm(src):
+def device_asm(src, extra=()):
     flags = [f for f in build.FLAGS if f not in ("-fPIC", "-shared")]
-    res = subprocess.run([HIPCC, *flags, "--cuda-device-only", "-S", src, "-o", "-"],
+    res = subprocess.run([HIPCC, *flags, *extra, "--cuda-device-only", "-S", src, "-o", "-"],
                          capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
     return res.stdout
@@ -46,10 +46,15 @@ SCALAR_WRITE = re.compile(r"^(s_store|s_scratch_store|s_buffer_store|s_atomic|s_
 PACKED_F32 = re.compile(r"^v_pk_(add|mul|fma)_f32")
 
 
+# every source as the library builds it, and the attention kernels' instrumented
+# build (phase stamps) as the stamp tool builds it
+CASES = [(os.path.basename(p)[:-4], ()) for p in sorted(build.sources())] + [("decode_bf16", ("-DMLA_STAMPS",))]
+
+
 @pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipcc") is None, reason="hipcc not found")
-@pytest.mark.parametrize("name", sorted(os.path.basename(p)[:-4] for p in build.sources()))
-def test_device_code_properties(name):
-    asm = device_asm(os.path.join(build.CSRC, name + ".hip"))
+@pytest.mark.parametrize("name,extra", CASES, ids=[n + ("-stamps" if e else "") for n, e in CASES])
+def test_device_code_properties(name, extra):
+    asm = device_asm(os.path.join(build.CSRC, name + ".hip"), extra)
     insts = list(instructions(asm))
     assert insts, "no instructions parsed"
     for k, s in enumerate(insts):
