@@ -70,6 +70,10 @@ constexpr int kMaxSplitsPerSeq = 1024;  // bound on a sequence's token ranges
 constexpr int kMinRaggedChunk = 256;   // tokens per range at least, ragged batches
 constexpr int kRaggedPerSlot = 2;      // ragged batches: workgroups per CU slot
 constexpr int kRowsRangeMin = 1024;     // see the fast form's choice below
+#ifndef MLA_FAST64_FORM
+#define MLA_FAST64_FORM kFormPingPong
+#endif
+constexpr int kFast64Form = MLA_FAST64_FORM;  // the fast form of 64-row workgroups
 
 struct Plan {
   int fast_form;     // kForm128 (rows a multiple of 128) or kFormRoles
@@ -97,8 +101,12 @@ Plan plan_bf16(const Resolved& r, const mla_decode_args* a) {
   // 78.6 against 84.4 us (DeepSeek-shaped) and 75.9 against 82.3 us (paged), while
   // the ragged two-query workload keeps 128-row ranges of ~1.5K tokens (455 against
   // 557 us).
-  p.fast_form = kFormRoles;
+  p.fast_form = kFast64Form;
+#ifndef MLA_NO_FORM128
   if (rows % 128 == 0 && a->num_splits == 0) {
+#else
+  if (false) {
+#endif
     const int64_t units = static_cast<int64_t>(a->batch) * (rows / 128);
     const int64_t c128 = ceil_div(L, std::min(ceil_div(target, units), ceil_div(L, kTile)));
     if (c128 >= kRowsRangeMin) p.fast_form = kForm128;

@@ -102,7 +102,8 @@ struct Ic {
 // last value pass and after its epilogue's stores have completed, and writes
 //   [0] entry, [1] first step's barrier, [2] last step's barrier, [3] barriers
 //   passed, [4] sum of the intervals between consecutive barriers, [5] shortest,
-//   [6] longest, [7] after the last value pass, [8] stores complete
+//   [6] longest, [7] after the last value pass, [8] stores complete, [9], [10] sums
+//   of the cycles from each step's barrier to the kernel's marks 0 and 1 ([11]: mark 2)
 // to stamp_buf[unit][wave][kStampSlots]. Product builds compile none of it.
 #ifdef MLA_STAMPS
 constexpr bool kStamps = true;
@@ -110,11 +111,12 @@ constexpr bool kStamps = true;
 constexpr bool kStamps = false;
 #endif
 constexpr int kStampUnits = 64, kStampSlots = 16;
+constexpr int kStampWaves = 8;  // records per unit (one per wave)
 struct StampRec {
-  uint64_t v[9];
+  uint64_t v[kStampSlots];
   __device__ __forceinline__ void begin() {
     v[0] = __builtin_amdgcn_s_memtime();
-    v[3] = v[4] = v[6] = 0;
+    for (int k = 1; k < kStampSlots; ++k) v[k] = 0;
     v[5] = ~0ull;
   }
   __device__ __forceinline__ void step() {  // right after a barrier
@@ -131,11 +133,15 @@ struct StampRec {
     ++v[3];
   }
   __device__ __forceinline__ void loop_end() { v[7] = __builtin_amdgcn_s_memtime(); }
+  // [9 + k] sums, over the steps, the cycles from the step's barrier to mark k
+  __device__ __forceinline__ void mark(int k) {
+    if (v[3] != 0) v[9 + k] += __builtin_amdgcn_s_memtime() - v[2];
+  }
   __device__ __forceinline__ void end(uint64_t* buf, int unit, int wave, int lane) {
     wait_vm<0>();
     v[8] = __builtin_amdgcn_s_memtime();
     if (unit < kStampUnits && lane == 0)
-      for (int k = 0; k < 9; ++k) buf[(static_cast<int64_t>(unit) * 4 + wave) * kStampSlots + k] = v[k];
+      for (int k = 0; k < kStampSlots; ++k) buf[(static_cast<int64_t>(unit) * kStampWaves + wave) * kStampSlots + k] = v[k];
   }
 };
 
@@ -152,6 +158,21 @@ __device__ __forceinline__ void mfma_v(f32x16& c, const u32x4& a, const u32x4& b
 __device__ __forceinline__ void mfma_v_last(f32x16& c, const u32x4& a, const u32x4& b) {
   asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 4"
       : "+v"(c) : "v"(a), "v"(b));
+}
+
+// v_mfma_f32_16x16x32_bf16 (4 passes) in VGPR form, for the eight-wave form's score
+// chains: as an opaque statement it keeps the chain's LDS fragment window as written
+// (the compiler shortens the window of the builtin form to two reads in flight).
+// The first of a chain takes a zero accumulator, the last waits out the result
+// latency (7 wait states for a 4-pass MFMA before VALU reads its result; 11 here).
+__device__ __forceinline__ void mfma16_first(f32x4& c, const u32x4& a, const u32x4& b) {
+  asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma16(f32x4& c, const u32x4& a, const u32x4& b) {
+  asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma16_last(f32x4& c, const u32x4& a, const u32x4& b) {
+  asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 2" : "+v"(c) : "v"(a), "v"(b));
 }
 
 // The same with the B operand in AGPRs (the precise form's low query halves).
@@ -829,6 +850,7 @@ __global__ __launch_bounds__(256) void decode_roles_kernel(DecodeArgs a) {
       if constexpr (!SC) {
         if (i + 1 < n_tiles) wait_vm<LOADS>();  // tile i has landed (tile i + 1 in flight)
         else wait_vm<0>();
+        if constexpr (kStamps) stamp.mark(2);
       }
       lds_barrier();  // tile i and P of tile i - 1 everywhere; tile i - 2 is free
       if constexpr (kStamps) stamp.step();
@@ -943,8 +965,406 @@ __global__ __launch_bounds__(256) void decode_roles_kernel(DecodeArgs a) {
   if constexpr (kStamps) stamp.end(a.stamps, u, w, l);
 }
 
+// Eight-wave form for 64 query rows per workgroup (the unit of the role-split form:
+// sequence, token range, two 32-row query blocks). Each SIMD hosts one score wave
+// and one value wave, so the matrix cores of a SIMD take one wave's MFMAs while the
+// other wave runs its softmax, its LDS traffic or waits for its tile loads to be
+// taken: overlap the four-wave forms could only get by interleaving code within
+// one wave.
+//
+// Score waves 0-3: wave s takes row block rb = s / 2 (32 rows: one query, 32 heads)
+// and token half th = s % 2 of every tile, as two 16-row sub-blocks on
+// v_mfma_f32_16x16x32_bf16 (A = 16 tokens x 32 columns of the tile, read from LDS
+// once and used by both sub-blocks; B = the rows' Q_cat, held in registers). Its
+// accumulators hold, in lane l, rows 16 sb + l % 16 and tokens 16 th + 4 (l / 16) +
+// 0..3. The two waves of a row block share each row's reference max: they exchange
+// their maxima of the range's first tile through LDS (the range's first tile is
+// where a row sees its first token, if it sees any), and their row sums at the end.
+// Each writes its half of P into the value MFMA's B-operand order.
+//
+// Value waves 4-7: wave 4 + v owns latent columns 128 v .. 128 v + 127 of all 64
+// rows (Oᵀ: 4 column blocks x 2 row blocks of 32x32 fp32) on v_mfma_f32_32x32x16_bf16,
+// with K = 16 tokens per k-step in their natural order, and issues a quarter of
+// every tile's loads at the start of the step.
+//
+// The pipeline, the restart rule, the masking and the output are those of the
+// role-split form: step i waits for tile i, passes the one barrier, issues tile i + 2
+// into the buffer of tile i - 2, scores tile i and publishes its P into buffer i % 2,
+// while the value waves run tile i - 1 from P buffer (i - 1) % 2.
+template <int DR>
+__global__ __launch_bounds__(512) void decode_pp_kernel(DecodeArgs a) {
+  constexpr int ROW = 512 + DR, ROWB = ROW * 2;
+  constexpr int KS = ROW / 32;                    // score k-steps (K = 32 each)
+  constexpr int KS16 = ROW / 16;                  // k-steps of the Q_cat block order
+  constexpr int TILE_BYTES = kTileT * ROWB;
+  constexpr int LOADS = 8 + (DR == 64 ? 1 : 0);   // 1 KiB loads per value wave per tile
+  constexpr int PBUF = 2 * 2 * 1024;              // P fragments [row block][k-step][lane]
+  __shared__ __attribute__((aligned(1024))) char s_tile0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char s_tile1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char s_tile2[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char s_tile3[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char s_p[2 * PBUF];
+  __shared__ float s_x[2][2][32];   // [row block][token half][row]: the first tile's row maxima
+  __shared__ float s_ms[2][2][32];  // ... the range's largest scores (restart references)
+  __shared__ float s_l[2][32];      // [row block][row]: row sums of token half 1
+  __shared__ int s_flag[4];
+  static_assert(4 * TILE_BYTES + 2 * PBUF + 2 * 4 * 32 * 4 + 2 * 32 * 4 + 16 <= 160 * 1024, "LDS");
+
+  const int tid = threadIdx.x, l = tid % 64;
+  const int w = __builtin_amdgcn_readfirstlane(tid / 64);  // wave index, uniform
+  const bool scorer = w < 4;
+  const int hgroups = (a.h * a.n_q) / 64;
+  const int HB = a.h / 32;
+  int u = blockIdx.x;
+  if ((a.units & 7) == 0) u = (blockIdx.x & 7) * (a.units >> 3) + (blockIdx.x >> 3);
+  StampRec stamp;
+  if constexpr (kStamps) stamp.begin();
+  const int pair = u / hgroups, hg = u - pair * hgroups;
+  const WorkItem item = a.list[pair];
+  if (item.b < 0) return;  // uniform: past the pairs of this launch
+  const int b = item.b, kv = item.kv;
+  const int t_begin = item.s * a.chunk;
+  const int t_end = min(t_begin + a.chunk, kv);
+  if (t_begin >= t_end || kv < a.n_q) return;  // not listed by the plan
+  const int n_tiles = (t_end - t_begin + kTileT - 1) / kTileT;
+  const int bound = min(t_end - 1, kv - a.n_q);
+  const int first_masked = bound - t_begin - (kTileT - 1) >= 0 ? (bound - t_begin - (kTileT - 1)) / kTileT + 1 : 0;
+  const int64_t prow0 = static_cast<int64_t>(item.p) * a.n_q;
+  auto tile_ptr = [&](auto kc) __attribute__((always_inline)) -> char* {
+    constexpr int K = decltype(kc)::value;
+    if constexpr (K == 0) return s_tile0;
+    else if constexpr (K == 1) return s_tile1;
+    else if constexpr (K == 2) return s_tile2;
+    else return s_tile3;
+  };
+
+  auto run = [&](auto role) __attribute__((always_inline)) {
+    constexpr bool SC = decltype(role)::value != 0;
+    // ---------------- score-wave state
+    const int rb = (w >> 1) & 1, th = w & 1;
+    const int qb_own = 2 * hg + rb;
+    const int j_own = qb_own / HB;
+    const int vis_own = kv - a.n_q + j_own;
+    u32x4 qf[SC ? 2 : 1][SC ? KS : 1];  // Q_cat of sub-blocks 0, 1 (B operand, K = 32)
+    float m_ref[2] = {-INFINITY, -INFINITY}, m_seen[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+    uint64_t ovr = 0;
+    // score A operand: token 16 th + l % 16, chunk 4 (ks % 2) + l / 16 of group ks / 2
+    int sa_off[2];
+    {
+      const int t = 16 * th + (l & 15), sw = swz(t);
+#pragma unroll
+      for (int par = 0; par < 2; ++par) sa_off[par] = t * 128 + (((4 * par + (l >> 4)) ^ sw) << 4);
+    }
+    // ---------------- value-wave state
+    const int vw = w & 3;
+    f32x16 acc[SC ? 1 : 8];  // Oᵀ: acc[cb * 2 + rb], column block 4 vw + cb
+    int pg_next = 0;
+    uint32_t ld_adj[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int t = 8 * q + (l >> 3);
+      ld_adj[q] = static_cast<uint32_t>(t * ROWB + (((l & 7) ^ swz(t)) << 4) - 1024 * q);
+    }
+    // value A operand (transposed reads), tokens in natural order: K index 8 h + e
+    // (h = l / 32) of value k-step kk is token 16 kk + 8 h + e. 16-lane group g, lane i
+    // reads row 8 (g / 2) + 4 sec + i / 4 and columns 16 (g % 2) + 4 (i % 4) of a
+    // 32-column block (sec 0: e = 0..3, sec 1: e = 4..7).
+    int va_off[2][2];
+    {
+      const int g = l >> 4, i = l & 15;
+#pragma unroll
+      for (int sec = 0; sec < 2; ++sec) {
+        const int t = 8 * (g >> 1) + 4 * sec + (i >> 2);
+        const int sw = swz(t);
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+          const int low = 2 * (g & 1) + ((i & 3) >> 1);
+          va_off[sec][par] = t * 128 + (((4 * par + low) ^ sw) << 4) + ((i & 1) << 3);
+        }
+      }
+    }
+    const char* cache = static_cast<const char*>(a.cache.data);
+    const bool paged = a.cache.block_table != nullptr;
+    const __attribute__((address_space(4))) int32_t* table =
+        (const __attribute__((address_space(4))) int32_t*)(a.cache.block_table);
+    auto page_id = [&](int it) __attribute__((always_inline)) -> int {
+      const int blk = (t_begin + it * kTileT) / a.cache.block_size;
+      const int id = table[static_cast<int64_t>(b) * a.cache.max_blocks + blk];
+      return (id < 0 || id >= a.cache.n_blocks) ? 0 : id;
+    };
+    auto tile_rsrc = [&](int it) __attribute__((always_inline)) -> u32x4 {
+      const int t0 = t_begin + it * kTileT;
+      const char* base;
+      if (!paged) {
+        base = cache + (static_cast<int64_t>(b) * a.cache.t_max + t0) * ROWB;
+      } else {
+        base = cache + (static_cast<int64_t>(pg_next) * a.cache.block_size + t0 % a.cache.block_size) * ROWB;
+        if (it + 1 < n_tiles) pg_next = page_id(it + 1);
+      }
+      const uint64_t ba = reinterpret_cast<uint64_t>(base);
+      const uint32_t rows = static_cast<uint32_t>(min(kTileT, t_end - t0));
+      return u32x4{static_cast<uint32_t>(ba), static_cast<uint32_t>(ba >> 32) & 0xFFFFu,
+                   rows * static_cast<uint32_t>(ROWB), 0x00020000u};
+    };
+    // value wave vw loads column groups vw and vw + 4 whole (runs of four 1 KiB
+    // blocks) and, with the RoPE key, block vw of group 8
+    auto issue_tile = [&](int it, char* tile) __attribute__((always_inline)) {
+      const u32x4 rsrc = tile_rsrc(it);
+      const uint32_t base = lds_addr(tile);
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int G = vw + 4 * r;
+        dma_run<4>(rsrc, ld_adj, static_cast<uint32_t>(G * 128), base + G * 4096);
+      }
+      if constexpr (DR == 64)
+        dma_run<1>(rsrc, ld_adj + vw, static_cast<uint32_t>(8 * 128 + 1024 * vw), base + 8 * 4096 + 1024 * vw);
+    };
+
+    constexpr int SDEPTH = 6;
+    auto scores = [&](const char* tile, f32x4 (&sc)[2]) __attribute__((always_inline)) {
+      u32x4 fa[SDEPTH];
+      auto frag = [&](int ks) __attribute__((always_inline)) {
+        return *(lds_u32x4*)(lds_ptr(tile) + sa_off[ks & 1] + (ks >> 1) * 4096);
+      };
+#pragma unroll
+      for (int ks = 0; ks < SDEPTH; ++ks) fa[ks] = frag(ks);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          if (ks == 0) mfma16_first(sc[sb], fa[0], qf[sb][0]);
+          else if (ks + 1 < KS) mfma16(sc[sb], fa[ks % SDEPTH], qf[sb][ks]);
+          else mfma16_last(sc[sb], fa[ks % SDEPTH], qf[sb][ks]);
+        }
+        if (ks + SDEPTH < KS) fa[ks % SDEPTH] = frag(ks + SDEPTH);
+      }
+    };
+    // rows of this lane: 16 sb + l % 16; reduce over the four lanes holding a row
+    auto row_max = [&](float x) __attribute__((always_inline)) {
+      x = fmaxf(x, __shfl_xor(x, 16));
+      return fmaxf(x, __shfl_xor(x, 32));
+    };
+    auto row_sum = [&](float x) __attribute__((always_inline)) {
+      x += __shfl_xor(x, 16);
+      return x + __shfl_xor(x, 32);
+    };
+    auto pv = [&](const char* tile, const char* pbuf) __attribute__((always_inline)) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        u32x4 pb[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) pb[r] = *(lds_u32x4*)(lds_ptr(pbuf) + (r * 2 + kk) * 1024 + l * 16);
+        i16x8 fr[4];
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          const int gcb = 4 * vw + cb;
+          lds_char* tb = lds_ptr(tile) + kk * 16 * 128 + (gcb >> 1) * 4096;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tb + va_off[0][gcb & 1]));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tb + va_off[1][gcb & 1]));
+          fr[cb] = i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int r = 0; r < 2; ++r)
+            acc[cb * 2 + r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fr[cb]), as_bf16x8(pb[r]),
+                                                                      acc[cb * 2 + r], 0, 0, 0);
+      }
+    };
+    auto vstep = [&](auto kc, auto first, int i, bool allow_restart) __attribute__((always_inline)) {
+      constexpr int K = decltype(kc)::value;
+      constexpr bool FIRST = decltype(first)::value != 0;
+      if constexpr (!SC) {
+        if (i + 1 < n_tiles) wait_vm<LOADS>();  // tile i has landed (tile i + 1 in flight)
+        else wait_vm<0>();
+        if constexpr (kStamps) stamp.mark(2);
+      }
+      lds_barrier();  // tile i and P of tile i - 1 everywhere; tile i - 2 is free
+      if constexpr (kStamps) stamp.step();
+      if constexpr (!SC) {
+        if (i + 2 < n_tiles) issue_tile(i + 2, tile_ptr(Ic<(K + 2) % 4>{}));
+        if constexpr (kStamps) stamp.mark(0);
+        if constexpr (FIRST) {
+          lds_barrier();  // the score waves' exchange of row maxima
+        } else {
+          pv(tile_ptr(Ic<(K + 3) % 4>{}), s_p + ((K + 1) & 1) * PBUF);
+          if constexpr (kStamps) stamp.mark(1);
+        }
+      } else {
+        f32x4 sc[2];
+        scores(tile_ptr(kc), sc);
+        if (i >= first_masked) {  // uniform
+          const int lim = min(t_end - 1, vis_own);
+          const int t0 = t_begin + i * kTileT + 16 * th + 4 * (l >> 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) sc[sb][e] = t0 + e > lim ? -INFINITY : sc[sb][e];
+        }
+        float mx[2];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          mx[sb] = fmaxf(fmaxf(sc[sb][0], sc[sb][1]), fmaxf(sc[sb][2], sc[sb][3]));
+          m_seen[sb] = fmaxf(m_seen[sb], mx[sb]);
+        }
+        if constexpr (kStamps) stamp.mark(0);
+        if constexpr (FIRST) {
+          // the row maxima of the range's first tile, over both token halves
+          float rm[2];
+#pragma unroll
+          for (int sb = 0; sb < 2; ++sb) rm[sb] = row_max(mx[sb]);
+          if (l < 16) {
+            s_x[rb][th][l] = rm[0];
+            s_x[rb][th][16 + l] = rm[1];
+          }
+          lds_barrier();
+#pragma unroll
+          for (int sb = 0; sb < 2; ++sb) {
+            const float other = s_x[rb][th ^ 1][16 * sb + (l & 15)];
+            if (m_ref[sb] == -INFINITY) m_ref[sb] = fmaxf(rm[sb], other);
+          }
+        }
+        bool overrun = false;
+        u32x2 pk[2];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          overrun |= allow_restart && mx[sb] > m_ref[sb] + kHeadroom;
+          const float mref = m_ref[sb] == -INFINITY ? 0.f : m_ref[sb];
+          const float p0 = fast_exp2(sc[sb][0] - mref), p1 = fast_exp2(sc[sb][1] - mref);
+          const float p2 = fast_exp2(sc[sb][2] - mref), p3 = fast_exp2(sc[sb][3] - mref);
+          pk[sb] = u32x2{pack_bf16x2(p0, p1), pack_bf16x2(p2, p3)};
+          l_run[sb] += (p0 + p1) + (p2 + p3);
+        }
+        ovr |= __builtin_amdgcn_ballot_w64(overrun);
+        // P[rb][k-step th][lane 16 sb + l % 16 + 32 (l / 32)][4 ((l / 16) % 2) + e]
+        char* pd = s_p + (K & 1) * PBUF + (rb * 2 + th) * 1024 + ((l >> 5) * 32 + (l & 15)) * 16 + ((l >> 4) & 1) * 8;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) *(lds_u32x2*)(lds_ptr(pd) + sb * 16 * 16) = pk[sb];
+        if constexpr (kStamps) stamp.mark(1);
+      }
+    };
+    auto prologue = [&]() __attribute__((always_inline)) {
+      if constexpr (!SC) {
+        if (paged) pg_next = page_id(0);
+        if (0 < n_tiles) issue_tile(0, s_tile0);
+        if (1 < n_tiles) issue_tile(1, s_tile1);
+      }
+    };
+
+    prologue();
+    if constexpr (SC) {
+      // Q_cat block order: column c of head-in-block hi at k-step c / 16, lane
+      // hi + 32 ((c / 8) % 2), element c % 8; this lane's fragment of k-step ks,
+      // sub-block sb: head-in-block 16 sb + l % 16, columns 32 ks + 8 (l / 16) + 0..7.
+      // The compiler's wait before each fragment's first use lets the first score
+      // chain start while later fragments still arrive.
+      const u32x4* qp = reinterpret_cast<const u32x4*>(a.q_cat) +
+                        (static_cast<int64_t>(b) * a.n_q * HB + qb_own) * KS16 * 64 + (l >> 5) * 64 + (l & 15) +
+                        32 * ((l >> 4) & 1);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) qf[sb][ks] = qp[ks * 128 + 16 * sb];
+    }
+    for (int pass = 0;; ++pass) {
+      const bool allow_restart = pass < kMaxRestarts;
+      if constexpr (!SC) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] = f32x16{};
+      }
+      l_run[0] = l_run[1] = 0.f;
+      ovr = 0;
+      if (pass > 0) prologue();
+      vstep(Ic<0>{}, Ic<1>{}, 0, allow_restart);
+      for (int i = 1; i < n_tiles; i += 4) {
+#define MLA_PSTEP(KK, D) \
+  if (i + D < n_tiles) vstep(Ic<KK>{}, Ic<0>{}, i + D, allow_restart);
+        MLA_PSTEP(1, 0)
+        MLA_PSTEP(2, 1)
+        MLA_PSTEP(3, 2)
+        MLA_PSTEP(0, 3)
+#undef MLA_PSTEP
+      }
+      float ms[2] = {0.f, 0.f};
+      if constexpr (SC) {
+        if (l == 0) s_flag[w] = ovr != 0;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) ms[sb] = row_max(m_seen[sb]);
+        if (l < 16) {
+          s_ms[rb][th][l] = ms[0];
+          s_ms[rb][th][16 + l] = ms[1];
+        }
+      }
+      lds_barrier();  // P of the last tile, every flag and the score waves' m_seen
+      const bool restart = (s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3]) != 0;  // uniform
+      if (!restart) {
+        if constexpr (!SC) {
+          const int kl = (n_tiles - 1) & 3;
+          const char* lt = kl == 0 ? s_tile0 : kl == 1 ? s_tile1 : kl == 2 ? s_tile2 : s_tile3;
+          pv(lt, s_p + ((n_tiles - 1) & 1) * PBUF);
+        }
+        if constexpr (kStamps) stamp.loop_end();
+        break;
+      }
+      // restart the range with the largest score of each row as its reference
+      if constexpr (SC) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          m_ref[sb] = fmaxf(ms[sb], s_ms[rb][th ^ 1][16 * sb + (l & 15)]);
+          m_seen[sb] = -INFINITY;
+        }
+      } else {
+        wait_vm<0>();
+      }
+      lds_barrier();  // every wave's reads of the flags and maxima are done
+    }
+
+    // ---- epilogue: value waves store their columns of the partial O (fp32, straight
+    //      from the accumulators); the score waves of token half 1 hand their row sums
+    //      to those of half 0, which store (m, l)
+    float ls[2] = {0.f, 0.f};
+    if constexpr (SC) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) ls[sb] = row_sum(l_run[sb]);
+      if (th == 1 && l < 16) {
+        s_l[rb][l] = ls[0];
+        s_l[rb][16 + l] = ls[1];
+      }
+    }
+    lds_barrier();
+    if constexpr (!SC) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int qb = 2 * hg + r, j = qb / HB;
+        const int head = 32 * (qb - j * HB) + (l & 31);
+        float* dst = a.o_part + ((prow0 + j) * a.h + head) * 512 + 128 * vw + 4 * (l >> 5);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) {
+            const f32x16& o = acc[cb * 2 + r];
+            *reinterpret_cast<f32x4*>(dst + 32 * cb + 8 * v4) = f32x4{o[4 * v4], o[4 * v4 + 1], o[4 * v4 + 2], o[4 * v4 + 3]};
+          }
+      }
+    } else {
+      if (th == 0 && l < 16) {
+        const int hb = qb_own - j_own * HB;
+        float* ml = a.ml_part + ((prow0 + j_own) * a.h + 32 * hb + l) * 2;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          ml[32 * sb + 0] = m_ref[sb];
+          ml[32 * sb + 1] = ls[sb] + s_l[rb][16 * sb + l];
+        }
+      }
+    }
+  };
+  if (scorer) run(Ic<1>{});
+  else run(Ic<0>{});
+  if constexpr (kStamps) stamp.end(a.stamps, u, w, l);
+}
+
 #ifdef MLA_STAMPS
-__device__ uint64_t stamp_buf[kStampUnits * 4 * kStampSlots];
+__device__ uint64_t stamp_buf[kStampUnits * kStampWaves * kStampSlots];
 #endif
 
 hipError_t launch_decode_bf16(const DecodeArgs& a_in, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
@@ -968,6 +1388,10 @@ hipError_t launch_decode_bf16(const DecodeArgs& a_in, hipStream_t s, hipEvent_t 
   } else if (a.form == kFormRoles) {
     if (a.d_r == 64) MLA_LAUNCH((decode_roles_kernel<64, false>));
     else if (a.d_r == 0) MLA_LAUNCH((decode_roles_kernel<0, false>));
+    else return hipErrorInvalidValue;
+  } else if (a.form == kFormPingPong) {
+    if (a.d_r == 64) hipExtLaunchKernelGGL((decode_pp_kernel<64>), grid, dim3(512), 0, s, ev0, ev1, 0, a);
+    else if (a.d_r == 0) hipExtLaunchKernelGGL((decode_pp_kernel<0>), grid, dim3(512), 0, s, ev0, ev1, 0, a);
     else return hipErrorInvalidValue;
   } else if (a.form == kFormPrecise) {
     if (a.d_r == 64) MLA_LAUNCH((decode_roles_kernel<64, true>));

@@ -68,6 +68,7 @@ enum DecodeForm : int32_t {
   kForm128 = 0,       // 128 query rows per workgroup, one bf16 query (fast)
   kFormRoles = 1,     // role-split 64-row workgroups, one bf16 query (fast)
   kFormPrecise = 2,   // role-split 64-row workgroups, query and probabilities as hi + lo bf16
+  kFormPingPong = 3,  // eight-wave 64-row workgroups (a score and a value wave per SIMD), one bf16 query (fast)
 };
 
 struct DecodeArgs {

@@ -25,7 +25,7 @@ import sys
 import time
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-UNITS, WAVES, SLOTS = 64, 4, 16  # the stamp buffer's shape (kStampUnits, waves, kStampSlots)
+UNITS, WAVES, SLOTS = 64, 8, 16  # the stamp buffer's shape (kStampUnits, kStampWaves, kStampSlots)
 
 
 def build_stamped(out_dir: str) -> str:
@@ -105,8 +105,8 @@ def table(w, st, attn, product_ms=None):
     total = np.median([float(st[u, v, 8] - st[u, v, 0]) for u, v in valid])
     ghz = total / (kernel_ms * 1e6)  # the sampled workgroups span about the whole launch
     # role-split form: waves 0-1 score, waves 2-3 hold the values; 128-row form: every
-    # wave does both
-    roles = {"waves 0-1": (0, 1), "waves 2-3": (2, 3)}
+    # wave does both; eight-wave form: waves 0-3 score, waves 4-7 hold the values
+    roles = {"waves 0-1": (0, 1), "waves 2-3": (2, 3), "waves 4-7": (4, 5, 6, 7)}
     lines = ["| phase (cycles, mean over sampled workgroups) | " + " | ".join(roles) + " |",
              "|---|" + "---|" * len(roles)]
     rows = [("entry to the first step's barrier (Q, first tiles)", lambda s: s[1] - s[0]),
@@ -114,6 +114,12 @@ def table(w, st, attn, product_ms=None):
             ("one step (barrier to barrier), mean", lambda s: s[4] / max(1, s[3] - 1)),
             ("one step, shortest", lambda s: s[5]),
             ("one step, longest", lambda s: s[6]),
+            ("barrier to mark 0, mean per step (eight-wave form: scores done / loads issued)",
+             lambda s: s[9] / max(1, s[3])),
+            ("barrier to mark 1, mean per step (eight-wave form: P written / value MFMAs issued)",
+             lambda s: s[10] / max(1, s[3] - 1)),
+            ("barrier to mark 2, mean per step (eight-wave form: next tile landed)",
+             lambda s: s[11] / max(1, s[3] - 1)),
             ("last barrier to the end of the last value pass", lambda s: s[7] - s[2]),
             ("epilogue (partial rows stored and complete)", lambda s: s[8] - s[7]),
             ("entry to stores complete", lambda s: s[8] - s[0])]

@@ -364,6 +364,54 @@ def test_large_score_jump_restarts_the_range():
     check_bf16(out, ref, what="all heads after a score jump")
 
 
+def test_large_score_jump_restarts_a_fast_range():
+    """The same score jump in a sequence long enough for the fast attention form
+    (4300 tokens, 64-row workgroups, ranges of a few tiles): the first tile of
+    range 0 is shrunk, so head 0's scores in the range's second tile beat its first
+    tile by more than 64 (base 2) and the range restarts; every output must still
+    match the oracle."""
+    w = synth.make_workload(2, batch=1, ctx=4300)
+    t = synth.draw(w)
+    qn = synth.bf16_bits_to_f64(t["q_nope"])
+    qn[0, 0, 0] *= 60.0
+    t["q_nope"] = torch.from_numpy(qn).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    cl = synth.bf16_bits_to_f64(t["c_kv"])
+    cl[0, :32] *= 0.1
+    t["c_kv"] = torch.from_numpy(cl).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    c = synth.bf16_bits_to_f64(t["c_kv"])[0]
+    kr = oracle.cache_keys(d_r=64, k_r=t["k_r"], kv_lens=w.kv_lens)[0]
+    qa = synth.bf16_bits_to_f64(t["q_nope"])[0, 0, 0] @ synth.bf16_bits_to_f64(t["w_uk"])[:, :128].T
+    qr = oracle.rope(synth.bf16_bits_to_f64(t["q_r"])[0, 0, 0], 4300)
+    s = (c @ qa + kr @ qr) / np.sqrt(192) * np.log2(np.e)
+    say("  head 0: first-tile max %.1f, second-tile max %.1f" % (s[:32].max(), s[32:64].max()))
+    assert s[32:64].max() > s[:32].max() + 64
+    step = GpuStep(w, t)
+    out = step.decode().cpu().numpy().astype(np.float64)
+    ref, lse = oracle_out(w, t, want_lse=True)
+    check_bf16(out[:, :, :128], ref[:, :, :128], what="head 0 after a score jump (fast form)")
+    check_bf16(out, ref, what="all heads after a score jump (fast form)")
+    assert np.max(np.abs(step.lse.cpu().numpy() - lse)) <= 1e-2
+
+
+@pytest.mark.parametrize("cid,h,n_q,ctx", [(4, 32, 2, (4200, 4800)), (2, 64, 1, 4500), (5, 64, 1, 4200),
+                                           (4, 96, 2, (4100, 4400))])
+def test_fast_64_row_groups(cid, h, n_q, ctx):
+    """Sequences of 4096 tokens or more whose query rows take 64-row workgroups in the
+    fast form: 32 heads x 2 queries (two query blocks with different causal limits in
+    one workgroup), 64 heads x 1 query with and without the RoPE key, and 96 heads x
+    2 queries (three groups): every output and lse."""
+    w = synth.make_workload(cid, batch=3, ctx_range=ctx) if cid == 4 else synth.make_workload(cid, batch=2, ctx=ctx)
+    w.h = h
+    w.n_q = n_q
+    say("case %d h=%d B=%d n_q=%d kv=[%d..%d]" % (cid, h, w.batch, w.n_q, w.kv_lens.min(), w.kv_lens.max()))
+    t = synth.draw(w)
+    step = GpuStep(w, t)
+    out = step.decode().cpu().numpy().astype(np.float64)
+    ref, lse = oracle_out(w, t, want_lse=True)
+    check_bf16(out, ref, what="h=%d n_q=%d" % (h, n_q))
+    assert np.max(np.abs(step.lse.cpu().numpy() - lse)) <= 1e-2
+
+
 @pytest.mark.parametrize("batch,d_model", [(40, 8192), (72, 4096), (3, 2048)])
 def test_gate_row_blocks_and_widths(batch, d_model):
     """The gate GEMM over more than one 32-row block of queries, with K splits of 512
