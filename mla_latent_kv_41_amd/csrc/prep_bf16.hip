@@ -259,13 +259,14 @@ __global__ __launch_bounds__(512) void qprep_kernel(QPrepArgs a) {
     if (given) {
       load_given(mb, acc);
     } else {
-      if (mb > 0) load_rows(mb);
 #pragma unroll
       for (int i = 0; i < 8; ++i) *(lds_u32x4*)(lds_ptr(area) + (4 * i + (l >> 4)) * kQnB + (l & 15) * 16) = rows[i];
       // B fragment k-step ks: row l%32, k = 16ks + 8(l/32) + e
       u32x4 af[8];
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) af[ks] = *(lds_u32x4*)(lds_ptr(area) + (l & 31) * kQnB + (2 * ks + (l >> 5)) * 16);
+      // the next block's rows are in flight during this block's products and stores
+      if ((mb + 1) * 32 < a.M) load_rows(mb + 1);
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
         acc[cb] = f32x16{};
