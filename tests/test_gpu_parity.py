@@ -412,6 +412,20 @@ def test_fast_64_row_groups(cid, h, n_q, ctx):
     assert np.max(np.abs(step.lse.cpu().numpy() - lse)) <= 1e-2
 
 
+def test_fast_64_row_groups_forced_ranges():
+    """64 heads x 1 query at 4500 tokens (the eight-wave form) with the token ranges
+    forced to 1, 3 and 17 per sequence (range ends inside tiles, ranges of one
+    tile): every output against the oracle each time."""
+    w = synth.make_workload(2, batch=2, ctx=4500)
+    w.h = 64
+    t = synth.draw(w)
+    step = GpuStep(w, t)
+    ref = oracle_out(w, t)
+    for ns in (1, 3, 17, 141):
+        out = step.decode(num_splits=ns).cpu().numpy().astype(np.float64)
+        check_bf16(out, ref, what="h=64, %d ranges" % ns)
+
+
 @pytest.mark.parametrize("batch,d_model", [(40, 8192), (72, 4096), (3, 2048)])
 def test_gate_row_blocks_and_widths(batch, d_model):
     """The gate GEMM over more than one 32-row block of queries, with K splits of 512
