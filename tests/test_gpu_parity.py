@@ -393,6 +393,43 @@ def test_large_score_jump_restarts_a_fast_range():
     assert np.max(np.abs(step.lse.cpu().numpy() - lse)) <= 1e-2
 
 
+def test_large_score_jump_restarts_a_fast_range_without_rope():
+    """The score jump of the test above on the gated shape without the RoPE key
+    (h = 64, 4300 tokens in two forced ranges: the eight-wave form without the key
+    columns): head 0's second-tile scores beat its first tile by more than 64
+    (base 2) in the range that starts the sequence; every gated output must match
+    the oracle."""
+    w = synth.make_workload(5, batch=1, ctx=4300)
+    t = synth.draw(w)
+    qn = synth.bf16_bits_to_f64(t["q_nope"])
+    qn[0, 0, 0] *= 60.0
+    t["q_nope"] = torch.from_numpy(qn).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    cl = synth.bf16_bits_to_f64(t["c_kv"])
+    cl[0, :32] *= 0.1
+    t["c_kv"] = torch.from_numpy(cl).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    c = synth.bf16_bits_to_f64(t["c_kv"])[0]
+    qa = synth.bf16_bits_to_f64(t["q_nope"])[0, 0, 0] @ synth.bf16_bits_to_f64(t["w_uk"])[:, :128].T
+    s = (c @ qa) / np.sqrt(128) * np.log2(np.e)
+    say("  head 0: first-tile max %.1f, second-tile max %.1f" % (s[:32].max(), s[32:64].max()))
+    assert s[32:64].max() > s[:32].max() + 64
+    step = GpuStep(w, t)
+    out = step.decode(num_splits=2).cpu().numpy().astype(np.float64)
+    ref, lse = oracle_out(w, t, want_lse=True)
+    check_bf16(out[:, :, :128], ref[:, :, :128], what="head 0 after a score jump (no RoPE)")
+    check_bf16(out, ref, what="all heads after a score jump (no RoPE)")
+    lse_gpu = step.lse.cpu().numpy()
+    assert np.max(np.abs(lse_gpu[:, :, 1:] - lse[:, :, 1:])) <= 1e-2
+    # head 0's scores are ~60x the others' (its lse is ~113), so the one rounding the
+    # method takes on the query (the scaled absorbed query to bf16, RNE) moves its
+    # lse by more than 1e-2: compare it with the lse of that rounded query, exact
+    # otherwise (fp64 here)
+    q = torch.from_numpy(qa * (np.log2(np.e) / np.sqrt(128))).to(torch.bfloat16).double().numpy()
+    sc = c[:int(w.kv_lens[0])] @ q
+    lse_q = (sc.max() + np.log2(np.exp2(sc - sc.max()).sum())) * np.log(2)
+    say("  head 0 lse: GPU %.6f, exact %.6f, bf16-query emulation %.6f" % (lse_gpu[0, 0, 0], lse[0, 0, 0], lse_q))
+    assert abs(lse_gpu[0, 0, 0] - lse_q) <= 2e-3
+
+
 @pytest.mark.parametrize("cid,h,n_q,ctx", [(4, 32, 2, (4200, 4800)), (2, 64, 1, 4500), (5, 64, 1, 4200),
                                            (4, 96, 2, (4100, 4400))])
 def test_fast_64_row_groups(cid, h, n_q, ctx):
