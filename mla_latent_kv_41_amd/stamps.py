@@ -9,6 +9,8 @@ the last attention launch as a markdown table.
     python -m mla_latent_kv_41_amd.stamps --build DIR            # build only (CPU)
     python -m mla_latent_kv_41_amd.stamps --lib DIR/libmla.so --config 2 [--write FILE]
 
+    python -m mla_latent_kv_41_amd.stamps --time-only --config 2 --copies 1   # product build
+
 Each stamp costs one scalar round trip where the wave has no LDS operation
 outstanding, so the stamped kernel runs a little slower than the product build;
 the table gives both kernel times. Three copies of (cache, weights) are decoded in
@@ -56,9 +58,10 @@ def _events(n):
     return hip, pairs, elapsed
 
 
-def run(config: int, steps: int, num_splits: int = 0):
+def run(config: int, steps: int, num_splits: int = 0, copies: int = 3):
     """Decode steps through the loaded (stamped) library; returns the stamp buffer of
-    the last step and the attention times (ms) of the timed steps."""
+    the last step and the attention times (ms) of the timed steps. `copies` copies
+    of (cache, weights) are decoded in turn."""
     import numpy as np
     import torch
     from . import mla, synth
@@ -67,19 +70,19 @@ def run(config: int, steps: int, num_splits: int = 0):
     stamped = hasattr(L, "mla_stamps_buffer")
     w = synth.make_workload(config)
     t = synth.draw(w)
-    # three copies of (cache, weights) in turn, as the benchmark does, so the
-    # memory-side cache cannot hold the working set
-    copies = [GpuStep(w, t, poison=False) for _ in range(3)]
-    for c in copies[1:]:
-        c.q_nope, c.q_rope, c.out, c.lse = copies[0].q_nope, copies[0].q_rope, copies[0].out, copies[0].lse
+    # by default three copies of (cache, weights) in turn, as the benchmark does, so
+    # the memory-side cache cannot hold the working set; one copy lets it
+    steps_on = [GpuStep(w, t, poison=False) for _ in range(copies)]
+    for c in steps_on[1:]:
+        c.q_nope, c.q_rope, c.out, c.lse = steps_on[0].q_nope, steps_on[0].q_rope, steps_on[0].out, steps_on[0].lse
     hip, pairs, elapsed = _events(steps)
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < 0.5:  # clock ramp
         for k in range(32):
-            copies[k % 3].decode(num_splits=num_splits)
+            steps_on[k % copies].decode(num_splits=num_splits)
         torch.cuda.synchronize()
     for k in range(steps):
-        copies[k % 3].decode(num_splits=num_splits, events=pairs[k])
+        steps_on[k % copies].decode(num_splits=num_splits, events=pairs[k])
     torch.cuda.synchronize()
     attn = [elapsed(p) for p in pairs]
     if not stamped:
@@ -149,12 +152,17 @@ def main():
     ap.add_argument("--write", metavar="FILE", help="also write the table, with this command, to FILE")
     ap.add_argument("--time-only", action="store_true",
                     help="print the median attention time (ms) of the loaded library and exit")
+    ap.add_argument("--copies", type=int, default=3,
+                    help="with --time-only: copies of (cache, weights) decoded in turn (1 lets the "
+                         "memory-side cache hold one copy's working set)")
     args = ap.parse_args()
     if args.build:
         print(build_stamped(args.build))
         return
     if args.time_only:
-        _, _, attn = run(args.config, args.steps, args.num_splits)
+        if args.copies < 1:
+            ap.error("--copies must be at least 1")
+        _, _, attn = run(args.config, args.steps, args.num_splits, args.copies)
         print("attention_ms %.6f" % statistics.median(attn))
         return
     if not args.lib:

@@ -105,3 +105,21 @@ def test_kernels_use_no_scratch(name):
         assert set(v) == {"private_segment_fixed_size", "vgpr_spill_count"}, (k, v)  # both parsed
         assert v["private_segment_fixed_size"] == 0, (k, v)
         assert v["vgpr_spill_count"] == 0, (k, v)
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipcc") is None, reason="hipcc not found")
+def test_rate_microbenchmark_builds():
+    """The per-CU rate microbenchmark compiles for gfx950 under the library's flags,
+    with the same device-code rules (its direct-to-LDS loads write M0 themselves)."""
+    from mla_latent_kv_41_amd import rates
+    asm = device_asm(rates.SRC)
+    insts = list(instructions(asm))
+    assert any(s.startswith("buffer_load_dwordx4") and s.endswith(" lds") for s in insts)
+    assert any(s.startswith("v_mfma_f32_32x32x16_bf16") for s in insts)
+    assert any(s.startswith("v_mfma_f32_16x16x32_bf16") for s in insts)
+    for s in insts:
+        mnem = s.split()[0]
+        assert not IMPLICIT_M0.match(mnem), s
+        assert not SCALAR_WRITE.match(mnem), s
+        assert not PACKED_F32.match(mnem), s
+    assert not re.search(r"(vgpr_spill_count|private_segment_fixed_size):\s+[1-9]", asm)
