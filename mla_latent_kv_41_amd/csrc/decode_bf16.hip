@@ -33,11 +33,13 @@
 //
 // LDS tile layout: the 576 (or 512) columns are cut into groups of 64 (128 bytes,
 // eight 16-byte chunks); group G holds all 32 rows, row t at G*4096 + t*128, and
-// chunk k of the group at position k ^ swz(t), swz(t) = ((u & 1) << 2) | (u >> 1)
-// with u = (t >> 1) & 7. The 16-row column reads of the score operand and the
-// 4-row transposed reads of the value operand are then free of bank conflicts,
-// and each 1 KiB wave load (8 rows x one group) has a per-lane offset that takes
-// only two values.
+// chunk k of the group at position k ^ swz(t), swz(t) = (t >> 1) & 7: rows 2u and
+// 2u + 1 (128 bytes apart) share a permutation, and the eight pairs of 16 rows use
+// eight different ones. The score operand's column reads are then free of bank
+// conflicts both as 32 rows x one chunk per half wave (128-row and role-split forms)
+// and as 16 rows x two chunks (eight-wave form): 243-249 B/cycle per CU for
+// ds_read_b128, where the eight-wave reads under the earlier pair-interleaved
+// permutation ran at 128.
 //
 // Softmax state is kept in base-2 units (Q_cat carries scale * log2 e). Each row's
 // reference max is fixed at the first tile where the row sees a token, so the
@@ -70,10 +72,7 @@ constexpr int kTileT = 32;    // tokens per tile
 constexpr float kHeadroom = 64.0f;  // largest score - reference allowed (base-2 units)
 constexpr int kMaxRestarts = 8;
 
-__device__ __forceinline__ int swz(int t) {
-  const int u = (t >> 1) & 7;
-  return ((u & 1) << 2) | (u >> 1);
-}
+__device__ __forceinline__ int swz(int t) { return (t >> 1) & 7; }
 
 template <int NW, int DR>
 struct Cfg {
