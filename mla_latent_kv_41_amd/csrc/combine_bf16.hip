@@ -6,9 +6,10 @@
 //   M = max_s m_s,  L = Σ_s 2^(m_s - M) l_s,  o_lat = Σ_s 2^(m_s - M) O_s / L,
 //   lse = (M + log2 L) ln 2 (natural-log units).
 // Up-projection (MLA tutorial page §3.1 and the `bhsc,hdc->bhsd` einsum of §5.1):
-// out[m, i*128 + d] = o_lat[m, i, :] · W_UV_i[:, d], on v_mfma_f32_32x32x16_bf16
-// with o_lat entering as a hi + lo pair of bf16 rows (about 16 significant bits),
-// stored once per output element.
+// out[m, i*128 + d] = o_lat[m, i, :] · W_UV_i[:, d], on v_mfma_f32_16x16x32_bf16
+// (16 query rows per block, the most a workgroup merges) with o_lat entering as a
+// hi + lo pair of bf16 rows (about 16 significant bits), stored once per output
+// element.
 // Gate (Gated-MLA page §2.6): out *= sigmoid(g), g = x · W_G per channel of the
 // concatenated heads.
 #include "common.hpp"
@@ -59,11 +60,10 @@ __device__ __forceinline__ void to_bf16_pair(const float (&x)[N], uint32_t (&hi)
 // The first NB partial rows of every row go out at once, further ones NB at a time;
 // ranges merge in a fixed order.
 //
-// Up-projection, on v_mfma_f32_32x32x16_bf16: the merged rows enter as hi + lo pairs
+// Up-projection, on v_mfma_f32_16x16x32_bf16: the merged rows enter as hi + lo pairs
 // of bf16 rows from LDS (rows past the workgroup's read as zeros). Wave w computes the
-// 32 output columns of block w % 4 over latent half w / 4 (its 16 W_UV_i fragments
-// are loaded first); waves 4-7 hand their sums to waves 0-3 through LDS, which add
-// them, apply the gate and store.
+// 16 output columns of block w over all 512 latent columns (its 16 W_UV_i fragments
+// are loaded first), applies the gate and stores.
 template <int WPR, int RPW>
 __global__ __launch_bounds__(kWaves * 64) void combine_kernel(CombineArgs a) {
   constexpr int VW = 8 / WPR;              // floats per lane of a row
@@ -72,7 +72,6 @@ __global__ __launch_bounds__(kWaves * 64) void combine_kernel(CombineArgs a) {
   using V = typename VecT<VW>::T;
   __shared__ __attribute__((aligned(16))) char s_hi[kMaxRows * kAStride];
   __shared__ __attribute__((aligned(16))) char s_lo[kMaxRows * kAStride];
-  __shared__ __attribute__((aligned(16))) float s_x[4][8][64];
   const int i = blockIdx.x, mb = blockIdx.y;
   const int tid = threadIdx.x, l = tid % 64;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -82,12 +81,11 @@ __global__ __launch_bounds__(kWaves * 64) void combine_kernel(CombineArgs a) {
   const int rows = min(R, M - m0);
   const int64_t rstride = static_cast<int64_t>(a.n_q) * a.h;  // partial rows per range
   const bool latent = a.o_lat != nullptr;
-  const int cb = w & 3, kh = w >> 2;
 
-  // W_UV_i fragments of column block cb, the 16 k-steps of latent half kh
+  // W_UV_i fragments of output column block w, the 16 k-steps of 32 latent columns
   u32x4 bfr[16];
   if (!latent) {
-    const u32x4* wv = reinterpret_cast<const u32x4*>(a.w_uv_pk) + ((static_cast<int64_t>(i) * 4 + cb) * 32 + 16 * kh) * 64 + l;
+    const u32x4* wv = reinterpret_cast<const u32x4*>(a.w_uv_pk) + ((static_cast<int64_t>(i) * kWaves + w) * 16) * 64 + l;
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) bfr[ks] = wv[ks * 64];
   }
@@ -183,37 +181,32 @@ __global__ __launch_bounds__(kWaves * 64) void combine_kernel(CombineArgs a) {
   if (latent) return;  // uniform: no up-projection in latent mode
   __syncthreads();
 
-  // ---- (o_hi + o_lo)[rows][half kh] · W_UV_i[half kh][32 cb + ..]; A row l%32 (zero
-  //      past the workgroup's rows), k = 16 ks + 8 (l/32) + e
-  f32x16 acc = {};
-  const int ar = l & 31;
+  // ---- (o_hi + o_lo)[rows][:] · W_UV_i[:][16 w + ..]; A row l%16 (zero past the
+  //      workgroup's rows), k = 32 ks + 8 (l/16) + e; the hi and lo products run as
+  //      two accumulation chains, added at the end
+  f32x4 acc_h = {}, acc_l = {};
+  const int ar = l & 15;
   const bool arow = ar < rows;
-  const int aoff = ar * kAStride + (l >> 5) * 16 + kh * 512;
+  const int aoff = ar * kAStride + (l >> 4) * 16;
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks) {
     u32x4 ah = {0u, 0u, 0u, 0u}, al = {0u, 0u, 0u, 0u};
     if (arow) {
-      ah = *(lds_u32x4*)(lds_ptr(s_hi) + aoff + ks * 32);
-      al = *(lds_u32x4*)(lds_ptr(s_lo) + aoff + ks * 32);
+      ah = *(lds_u32x4*)(lds_ptr(s_hi) + aoff + ks * 64);
+      al = *(lds_u32x4*)(lds_ptr(s_lo) + aoff + ks * 64);
     }
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ah), as_bf16x8(bfr[ks]), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(al), as_bf16x8(bfr[ks]), acc, 0, 0, 0);
+    acc_h = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah), as_bf16x8(bfr[ks]), acc_h, 0, 0, 0);
+    acc_l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al), as_bf16x8(bfr[ks]), acc_l, 0, 0, 0);
   }
-  // rows 0 .. 15 of the 32x32 block are values 0 .. 7: row 8 (v / 4) + 4 (l / 32) + v % 4
-  if (kh == 1) {
-#pragma unroll
-    for (int v8 = 0; v8 < 8; ++v8) s_x[cb][v8][l] = acc[v8];
-  }
-  __syncthreads();
-  if (kh == 1) return;
+  // D lane l: output column 16 w + l % 16, rows 4 (l / 16) + v
   const int width = a.h * 128;
-  const int col = i * 128 + 32 * cb + (l & 31);
+  const int col = i * 128 + 16 * w + (l & 15);
 #pragma unroll
-  for (int v8 = 0; v8 < 8; ++v8) {
-    const int r = 8 * (v8 / 4) + 4 * (l >> 5) + (v8 & 3);
+  for (int v = 0; v < 4; ++v) {
+    const int r = 4 * (l >> 4) + v;
     if (r >= rows) continue;
     const int m = m0 + r;
-    float ov = acc[v8] + s_x[cb][v8][l];
+    float ov = acc_h[v] + acc_l[v];
     if (a.gate) {  // out = sigmoid(g) o
       float g = 0.f;
       for (int ks = 0; ks < kGateSplit; ++ks) g += a.gate[(static_cast<int64_t>(ks) * M + m) * width + col];

@@ -8,8 +8,10 @@
 // by scale * log2(e), so the attention kernel works in base-2 exponent units.
 //
 // Packing (done once at load, tutorial §3.2): W_UK and W_UV are re-laid out per
-// head in the exact per-lane fragment order of v_mfma_f32_32x32x16_bf16, so every
-// weight load in the hot kernels is one contiguous 1 KiB wave transaction.
+// head in the exact per-lane fragment order of the matrix-core instruction that
+// consumes them (v_mfma_f32_32x32x16_bf16 for W_UK, v_mfma_f32_16x16x32_bf16 for
+// W_UV), so every weight load in the hot kernels is one contiguous 1 KiB wave
+// transaction.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -18,8 +20,8 @@ namespace mla {
 // Fragment order (64 lanes x 8 bf16 = 1 KiB per fragment):
 //   W_UK (B operand of D[m][c] = q_nope[m][:] · W_UK_i[c][:]):
 //     frag (i, nb < 16, ks < 8), lane l: W_UK[32nb + l%32][i*128 + 16ks + 8(l/32) + e]
-//   W_UV (B operand of D[m][d] = o_lat[m][:] · W_UV_i[:][d]):
-//     frag (i, nb < 4, ks < 32), lane l: W_UV[16ks + 8(l/32) + e][i*128 + 32nb + l%32]
+//   W_UV (B operand of the 16x16x32 product D[m][d] = o_lat[m][:] · W_UV_i[:][d]):
+//     frag (i, nb < 8, ks < 16), lane l: W_UV[32ks + 8(l/16) + e][i*128 + 16nb + l%16]
 __global__ void pack_kernel(const uint16_t* __restrict__ w_uk, const uint16_t* __restrict__ w_uv,
                             uint16_t* __restrict__ packed, int h) {
   const int64_t per = static_cast<int64_t>(h) * 8192;  // lanes per region
@@ -38,9 +40,9 @@ __global__ void pack_kernel(const uint16_t* __restrict__ w_uk, const uint16_t* _
     const int64_t gg = g - per;
     const int l = gg % 64;
     const int64_t f = gg / 64;
-    const int ks = f % 32, nb = (f / 32) % 4, i = static_cast<int>(f / 128);
-    const int64_t col = static_cast<int64_t>(i) * 128 + 32 * nb + l % 32;
-    for (int e = 0; e < 8; ++e) v[e] = w_uv[(16 * ks + 8 * (l / 32) + e) * width + col];
+    const int ks = f % 16, nb = (f / 16) % 8, i = static_cast<int>(f / 128);
+    const int64_t col = static_cast<int64_t>(i) * 128 + 16 * nb + l % 16;
+    for (int e = 0; e < 8; ++e) v[e] = w_uv[(32 * ks + 8 * (l / 16) + e) * width + col];
   }
   u32x4 o;
   for (int e = 0; e < 4; ++e) o[e] = static_cast<uint32_t>(v[2 * e]) | (static_cast<uint32_t>(v[2 * e + 1]) << 16);

@@ -25,13 +25,16 @@
 //            loads at each step, spin C cycles, wait for the previous tile, then a
 //            barrier. Launches rotate over three copies of the data (as the
 //            benchmark rotates caches), so the Infinity Cache does not hold them.
+//            Variants: the odd unit of each pair reads the shared tiles in an order
+//            rotated by `rot` tiles (so the two do not fetch the same lines at the
+//            same time), and D = 3 issues three tiles ahead instead of two.
 //
 // Rates are bytes or FLOPs per cycle per CU, taken from the slowest wave of each
 // launch. Every kernel holds at least 96 KiB of LDS, so no CU runs two of the 256
 // workgroups. Every access stays inside its array or buffer (offsets are masked to
 // the sizes below); the buffer loads carry a 64 KiB size bound as well.
 //
-//   hipcc --offload-arch=gfx950 -O3 rates.hip -o rates && ./rates
+//   hipcc --offload-arch=gfx950 -O3 rates.hip -o rates && ./rates   (./rates s: the sched lines only)
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -243,7 +246,8 @@ __global__ __launch_bounds__(256) void stream_rate(const char* src) {
   wait_vm<0>();
 }
 
-__global__ __launch_bounds__(512) void sched_rate(const char* src, int C, int share, uint64_t* rec) {
+template <int D>
+__global__ __launch_bounds__(512) void sched_rate(const char* src, int C, int share, int rot, uint64_t* rec) {
   __shared__ __attribute__((aligned(1024))) char tiles[4 * kTileBytes];
   const int l = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int u = (blockIdx.x & 7) * 32 + (blockIdx.x >> 3);  // contiguous units per XCD
@@ -252,27 +256,31 @@ __global__ __launch_bounds__(512) void sched_rate(const char* src, int C, int sh
                       static_cast<uint32_t>(kRangeBytes), 0x00020000u};
   const bool loader = w >= 4;
   const int lw = w - 4;
+  const int r0 = (u & 1) ? rot : 0;  // the odd unit of a pair starts rot tiles in
   auto issue = [&](int it) {
     const uint32_t tb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char*)tiles)) + (it & 3) * kTileBytes;
+    const int pt = (it + r0) & 31;
 #pragma unroll
-    for (int k = 0; k < 9; ++k) dma_1k(rsrc, tile_off(it, 9 * lw + k, l), tb + (9 * lw + k) * 1024);
+    for (int k = 0; k < 9; ++k) dma_1k(rsrc, tile_off(pt, 9 * lw + k, l), tb + (9 * lw + k) * 1024);
   };
+  // D tiles ahead: at step i the loads of tile i + D go into the buffer of tile
+  // i + D - 4 (the kernel's form is D = 2; D = 3 keeps a third tile in flight)
   if (loader) {
-    issue(0);
-    issue(1);
-    wait_vm<9>();
+    for (int k = 0; k < D; ++k) issue(k);
+    wait_vm<9 * (D - 1)>();
   }
   __syncthreads();
   uint64_t steps = 0, issued = 0;
   for (int i = 0; i < 32; ++i) {
     const uint64_t t0 = __builtin_amdgcn_s_memtime();
     if (loader) {
-      if (i + 2 < 32) issue(i + 2);
+      if (i + D < 32) issue(i + D);
       const uint64_t t1 = __builtin_amdgcn_s_memtime();
       issued += t1 - t0;
       while (__builtin_amdgcn_s_memtime() - t1 < static_cast<uint64_t>(C)) {
       }
-      if (i + 2 < 32) wait_vm<9>();
+      if (i + D < 32) wait_vm<9 * (D - 1)>();
+      else if (D == 3 && i + 2 < 32) wait_vm<9>();
       else wait_vm<0>();
     }
     __syncthreads();
@@ -384,7 +392,7 @@ static void run_stream(const char* src) {
   CHECK(hipEventDestroy(e1));
 }
 
-static void run_sched(const char* src, int64_t copy, int share, int C) {
+static void run_sched(const char* src, int64_t copy, int share, int C, int rot = 0, int D = 2) {
   uint64_t* rec;
   CHECK(hipMalloc(&rec, kBlocks * 16));
   hipEvent_t e0, e1;
@@ -397,7 +405,8 @@ static void run_sched(const char* src, int64_t copy, int share, int C) {
     // per launch, two pairs in turn (the buffer holds four)
     const char* base = src + (share ? (rep % 3) * copy : (rep % 2) * 2 * copy);
     CHECK(hipEventRecord(e0));
-    sched_rate<<<kBlocks, 512>>>(base, C, share, rec);
+    if (D == 3) sched_rate<3><<<kBlocks, 512>>>(base, C, share, rot, rec);
+    else sched_rate<2><<<kBlocks, 512>>>(base, C, share, rot, rec);
     CHECK(hipEventRecord(e1));
     CHECK(hipEventSynchronize(e1));
     float ms;
@@ -412,16 +421,18 @@ static void run_sched(const char* src, int64_t copy, int share, int C) {
     is += static_cast<double>(h[2 * k + 1]);
   }
   const double us = tot / (reps - 3) * 1e3, bytes = (share ? 128.0 : 256.0) * kRangeBytes;
-  printf("sched    %s ranges, C=%4d: %.1f us for %.0f MB (%.2f TB/s), step %.0f cycles, tile issue %.0f\n",
-         share ? "shared" : "distinct", C, us, bytes / 1e6, bytes / (us * 1e-6) / 1e12, st / (kBlocks * 32.0),
+  printf("sched    %s ranges, D=%d, C=%4d, rot %2d: %.1f us for %.0f MB (%.2f TB/s), step %.0f cycles, tile issue %.0f\n",
+         share ? "shared" : "distinct", D, C, rot, us, bytes / 1e6, bytes / (us * 1e-6) / 1e12, st / (kBlocks * 32.0),
          is / (kBlocks * 32.0));
   CHECK(hipEventDestroy(e0));
   CHECK(hipEventDestroy(e1));
   CHECK(hipFree(rec));
 }
 
-int main() {
+int main(int argc, char** argv) {
+  const bool only_sched = argc > 1 && argv[1][0] == 's';
   const int it = 2048;
+  if (!only_sched) {
   run("lds", lds_read<8>, 8, it, 8192.0, "B");
   run("mfma16", mfma_rate<4, 0>, 4, it, 4 * 16384.0, "FLOP");
   run("mfma16", mfma_rate<8, 0>, 8, it, 4 * 16384.0, "FLOP");
@@ -435,20 +446,30 @@ int main() {
   run("score32", score_read<0, 0>, 8, 1024, 16 * 1024.0, "B");
   run("score16", score_read<1, 0>, 8, 1024, 16 * 1024.0, "B");
   run("score16p", score_read<1, 1>, 8, 1024, 16 * 1024.0, "B");
+  }
   // 2 GiB for the stream; four copies of 128 ranges (604 MB) for the schedule
   const int64_t copy = 128 * kRangeBytes;
   const int64_t total = std::max<int64_t>(kBlocks * kStreamPerWg, 4 * copy);
   char* src;
   CHECK(hipMalloc(&src, total));
   CHECK(hipMemset(src, 0, total));
-  run_stream<1>(src);
-  run_stream<2>(src);
-  run_stream<4>(src);
-  run_stream<9>(src);
-  run_stream<18>(src);
+  if (!only_sched) {
+    run_stream<1>(src);
+    run_stream<2>(src);
+    run_stream<4>(src);
+    run_stream<9>(src);
+    run_stream<18>(src);
+  }
   run_sched(src, copy, 1, 0);
   run_sched(src, copy, 1, 800);
   run_sched(src, copy, 0, 800);
+  // the odd unit of each pair reads the shared tiles in a rotated order
+  for (int rot : {2, 16}) run_sched(src, copy, 1, 0, rot);
+  // a third tile in flight
+  run_sched(src, copy, 1, 0, 0, 3);
+  run_sched(src, copy, 1, 800, 0, 3);
+  run_sched(src, copy, 1, 1400, 0, 3);
+  run_sched(src, copy, 0, 800, 0, 3);
   CHECK(hipFree(src));
   return 0;
 }
