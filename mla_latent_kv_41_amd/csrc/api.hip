@@ -126,6 +126,49 @@ Plan plan_bf16(const Resolved& r, const mla_decode_args* a) {
     }
     ragged = total * 5 < static_cast<int64_t>(a->batch) * L * 4;
   }
+  // with host lengths: the precise form's tokens, and whether both forms run (the
+  // precise launch then gets ranges of its own, below)
+  int64_t prec_units = 0;
+  bool any_fast = false;
+  if (a->kv_lens_host) {
+    for (int b = 0; b < a->batch; ++b) {
+      const int64_t kv = std::min<int64_t>(a->kv_lens_host[b], L);
+      if (kv < kPreciseBelow) prec_units += kv * p.prec_groups;
+      else any_fast = true;
+    }
+  }
+  const bool own_precise = a->kv_lens_host && a->num_splits == 0 && any_fast && prec_units > 0;
+  // workgroups of a launch with ranges of ch tokens over the fast form's sequences
+  // (which 0), the precise form's (1) or all (2), from the host lengths
+  auto workgroups = [&](int64_t ch, int which) {
+    int64_t n = 0;
+    for (int b = 0; b < a->batch; ++b) {
+      const int64_t kv = std::min<int64_t>(a->kv_lens_host[b], L);
+      const bool prec = kv < kPreciseBelow;
+      if (kv < a->n_q || (which == 0 && prec) || (which == 1 && !prec)) continue;
+      n += ceil_div(kv, ch) * groups_of(kv);
+    }
+    return n;
+  };
+  // The shortest range length from `base` (a multiple of kTile) whose launch fits in
+  // `limit` workgroups. Every sequence's last range is a remainder, so ranges sized
+  // from the token total alone can leave a launch a few workgroups past its last full
+  // wave of the chip, and those run as one more wave (the ragged two-query workload's
+  // precise launch: 276 workgroups of at most 14 tiles, against 248 of at most 16 at
+  // 512-token ranges). Taken when under twice `base`, since two waves of `base`-token
+  // ranges cost no more.
+  auto fit = [&](int64_t base, int64_t limit, int which) -> int64_t {
+    const int64_t top = ceil_div(L, kTile) * kTile;
+    if (base >= top || workgroups(base, which) <= limit) return base;
+    int64_t lo = base / kTile, hi = top / kTile;  // workgroups(lo * kTile) > limit
+    if (workgroups(hi * kTile, which) > limit) return base;
+    while (hi - lo > 1) {
+      const int64_t mid = (lo + hi) / 2;
+      if (workgroups(mid * kTile, which) <= limit) hi = mid;
+      else lo = mid;
+    }
+    return hi * kTile < 2 * base ? hi * kTile : base;
+  };
   int64_t chunk;
   if (a->num_splits > 0) {
     chunk = ceil_div(L, a->num_splits);
@@ -137,29 +180,23 @@ Plan plan_bf16(const Resolved& r, const mla_decode_args* a) {
     // tokens, so the partials of a range stay well below the cache bytes it reads
     chunk = std::max<int64_t>(kMinRaggedChunk, ceil_div(total_units, kRaggedPerSlot * target));
   } else {
-    // one workgroup per slot when every sequence is as long as the longest
+    // at most one workgroup per slot when every sequence is as long as the longest:
+    // as many ranges per sequence as fit the chip whole (a few past it would run as
+    // a second wave)
     const int64_t units = static_cast<int64_t>(a->batch) * groups_of(L);
-    chunk = ceil_div(L, std::min(ceil_div(target, units), ceil_div(L, kTile)));
+    chunk = ceil_div(L, std::min(std::max<int64_t>(1, target / units), ceil_div(L, kTile)));
   }
   chunk = std::max(chunk, ceil_div(L, kMaxSplitsPerSeq));
-  chunk = ceil_div(chunk, kTile) * kTile;
-  p.chunk = static_cast<int>(std::min<int64_t>(chunk, ceil_div(L, kTile) * kTile));
+  chunk = std::min(ceil_div(chunk, kTile) * kTile, ceil_div(L, kTile) * kTile);
+  if (ragged && a->num_splits == 0) chunk = fit(chunk, kRaggedPerSlot * target, own_precise ? 0 : 2);
+  p.chunk = static_cast<int>(chunk);
   p.chunk_precise = p.chunk;
-  if (a->kv_lens_host && a->num_splits == 0) {
-    // when both forms run, the precise launch follows the fast one on its own: size
-    // its ranges so its sequences' units fill the chip once (at least kMinRaggedChunk
-    // tokens), rather than by the fast form's ranges
-    int64_t prec_units = 0;
-    bool any_fast = false;
-    for (int b = 0; b < a->batch; ++b) {
-      const int64_t kv = std::min<int64_t>(a->kv_lens_host[b], L);
-      if (kv < kPreciseBelow) prec_units += kv * p.prec_groups;
-      else any_fast = true;
-    }
-    if (any_fast && prec_units > 0) {
-      const int64_t c = std::max<int64_t>(kMinRaggedChunk, ceil_div(prec_units, target));
-      p.chunk_precise = static_cast<int>(std::min<int64_t>(ceil_div(c, kTile) * kTile, ceil_div(L, kTile) * kTile));
-    }
+  if (own_precise) {
+    // the precise launch follows the fast one on its own: its ranges are sized so its
+    // sequences' units fill the chip once (at least kMinRaggedChunk tokens), rather
+    // than by the fast form's ranges
+    const int64_t c = std::max<int64_t>(kMinRaggedChunk, ceil_div(prec_units, target));
+    p.chunk_precise = static_cast<int>(fit(std::min<int64_t>(ceil_div(c, kTile) * kTile, ceil_div(L, kTile) * kTile), target, 1));
   }
   if (a->kv_lens_host) {
     for (int b = 0; b < a->batch; ++b) {
