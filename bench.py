@@ -103,7 +103,9 @@ def config_desc(w):
     return d
 
 
-KERNEL_SOURCES = ("decode_bf16.hip", "common.hpp")  # the attention kernel and its device helpers
+# the attention kernels, their device helpers, and the planner that sizes their launches
+KERNEL_SOURCES = ("decode_bf16.hip", "common.hpp", "api.hip", "launch.hpp")
+KERNEL_SOURCES_TEXT = " + ".join("mla_latent_kv_41_amd/csrc/" + f for f in KERNEL_SOURCES)
 
 
 def kernel_source_hash():
@@ -426,7 +428,7 @@ def summarize_ds_trace(d):
     lines = ["# Kernel trace: DeepSeek-shaped decode (h=128, B=32, 4096+1 tokens)", "",
              "Command (from /tmp with TMPDIR=/tmp; the run includes the bench's clock-settling steps):",
              "", "    " + TRACE_CMD, "",
-             "Per-step kernels: qprep_kernel (query absorption + RoPE, output zeroing, the split plan), "
+             "Per-step kernels: qprep_kernel (query absorption + RoPE, the split plan), "
              "%s (split-K attention), combine_kernel (split merge + W_UV). "
              "append_kernel, pack_kernel and the fills belong to set-up." % kname, "",
              "| kernel | calls | average us | min us | max us | share |", "|---|---|---|---|---|---|"]
@@ -434,7 +436,7 @@ def summarize_ds_trace(d):
         lines.append("| `%s` | %s | %.2f | %.2f | %.2f | %.1f%% |" % (
             short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
-    lines += ["", "Attention kernel source sha256 (mla_latent_kv_41_amd/csrc/decode_bf16.hip + common.hpp): `%s`" % sha, ""]
+    lines += ["", "Attention kernel source sha256 (%s): `%s`" % (KERNEL_SOURCES_TEXT, sha), ""]
     open(os.path.join(prof, "decode_step_%s_kernel_trace.md" % w_name), "w").write("\n".join(lines))
 
 
@@ -461,8 +463,8 @@ def summarize_other(d):
             lines.append("| `%s` | %s | %.2f | %.2f | %.2f | %.1f%% |" % (
                 short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
                 float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
-        lines += ["", "Attention kernel source sha256 (mla_latent_kv_41_amd/csrc/decode_bf16.hip + common.hpp): `%s`"
-                  % line["attention_kernel_source_sha256"], ""]
+        lines += ["", "Attention kernel source sha256 (%s): `%s`"
+                  % (KERNEL_SOURCES_TEXT, line["attention_kernel_source_sha256"]), ""]
         open(os.path.join(prof, "decode_step_%s_kernel_trace.md" % wl), "w").write("\n".join(lines))
     for c in (2, 3, 4, 5):
         if os.path.isdir(os.path.join(d, "ctr_c%d" % c, "sq")):
@@ -513,7 +515,7 @@ def summarize_traffic(d, cfg):
              "device-to-device copy, dispatched as `__amd_rocclr_copyBuffer` with grid %d):" % (COPY_BYTES // 4096), ""]
     lines += ["    " + PMC_CMD.format(c=c, cfg=cfg) for c in ("FETCH_SIZE", "WRITE_SIZE")]
     lines += ["", "Summarised with `python3 bench.py --summarize-profiles <out>`.", "",
-              "Attention kernel source sha256 (mla_latent_kv_41_amd/csrc/decode_bf16.hip + common.hpp): `%s`" % sha, "",
+              "Attention kernel source sha256 (%s): `%s`" % (KERNEL_SOURCES_TEXT, sha), "",
               "| kernel | grid | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB |", "|---|---|---|---|---|"]
     for (n, g), cs in sorted(vals.items(), key=lambda kv: -sum(kv[1].get("FETCH_SIZE", [0])) / max(1, len(kv[1].get("FETCH_SIZE", [0])))):
         fs = cs.get("FETCH_SIZE", [float("nan")])
