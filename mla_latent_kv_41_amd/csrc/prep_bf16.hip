@@ -138,7 +138,7 @@ __device__ void build_plan(const PlanArgs& p, int l) {
 // Waves 4-7 (side work, concurrent with the product's loads): rotate the q_R of
 // query rows m = nb (mod 8) of these heads. The rotation angle depends on
 // the row and the pair only: each half wave takes one row, lane k forms the sine and
-// cosine of pair k once, and the 4 heads' chunks fetch them by lane shuffles. Wave 4
+// cosine of pair k once, and the 4 heads' chunks fetch them by lane shuffles. Wave 7
 // of workgroup (0, 0) first builds the split plan.
 constexpr int kQHeads = 4;
 constexpr int kQColBlocks = 8;
@@ -165,7 +165,10 @@ __global__ __launch_bounds__(512) void qprep_kernel(QPrepArgs a) {
   if (w >= kQHeads) {
     // ================= side work: waves 4-7 =================
     const int sw = w - kQHeads;
-    if (g == 0 && nb == 0 && sw == 0) build_plan(a.plan, l);
+    // the plan goes to the side wave with the fewest rotation rows (wave 7 takes rows
+    // from t = 6 on, none when M <= 48), so no wave builds the plan and then waits on
+    // the loads of its rows
+    if (g == 0 && nb == 0 && sw == kQHeads - 1) build_plan(a.plan, l);
     const int srows = a.M > nb ? (a.M - nb + kQColBlocks - 1) / kQColBlocks : 0;
     // RoPE of q_R: half wave hf of wave sw takes side row t = 8u + 2sw + hf (u = 0, 1, ..),
     // query row m = nb + 8t. Pair k (columns 2k, 2k + 1) turns by pos * inv_freq[k], the
