@@ -217,6 +217,14 @@ __device__ __forceinline__ void dma_1k(const u32x4& rsrc, uint32_t voff, uint32_
 }
 // buffer offset of lane l in load r (0 .. 35) of tile `tile`: rows 8 (r % 4) + l / 8,
 // column group r / 4, chunk l % 8
+// a one-dword direct-to-LDS load per lane (64 lines per wave instruction): an L2
+// prefetch whose data lands in a sink nothing reads
+__device__ __forceinline__ void dma_4b(const u32x4& rsrc, uint32_t voff, uint32_t lds) {
+  uint32_t m = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("" : "+s"(m));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m), "v"(voff), "s"(rsrc)
+               : "m0");
+}
 __device__ __forceinline__ uint32_t tile_off(int tile, int r, int l) {
   return static_cast<uint32_t>(tile) * 36864u + (8 * (r % 4) + (l >> 3)) * 1152u + (r / 4) * 128u + (l & 7) * 16u;
 }
@@ -246,9 +254,10 @@ __global__ __launch_bounds__(256) void stream_rate(const char* src) {
   wait_vm<0>();
 }
 
-template <int D>
+template <int D, int PF>
 __global__ __launch_bounds__(512) void sched_rate(const char* src, int C, int share, int rot, uint64_t* rec) {
   __shared__ __attribute__((aligned(1024))) char tiles[4 * kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sink[4 * 256];
   const int l = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int u = (blockIdx.x & 7) * 32 + (blockIdx.x >> 3);  // contiguous units per XCD
   const uint64_t ba = reinterpret_cast<uint64_t>(src + (share ? u / 2 : u) * kRangeBytes);
@@ -263,6 +272,18 @@ __global__ __launch_bounds__(512) void sched_rate(const char* src, int C, int sh
 #pragma unroll
     for (int k = 0; k < 9; ++k) dma_1k(rsrc, tile_off(pt, 9 * lw + k, l), tb + (9 * lw + k) * 1024);
   };
+  // PF > 0: with the tile loads of step i, each unit of the pair also touches its half
+  // of the lines (rows 16 (u & 1) .. + 15, all nine 128-byte groups) of tile
+  // i + D + PF, one dword per line: lane j < 36 of loader wave lw takes line
+  // 36 lw + j, the other lanes repeat line 36 lw
+  auto prefetch = [&](int it) {
+    const int pt = min(it, 31);
+    const int q = 36 * lw + (l < 36 ? l : 0);
+    const uint32_t off = static_cast<uint32_t>(pt) * 36864u + static_cast<uint32_t>(16 * (u & 1) + q / 9) * 1152u +
+                         static_cast<uint32_t>(q % 9) * 128u;
+    const uint32_t sb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char*)sink)) + lw * 256;
+    dma_4b(rsrc, off, sb);
+  };
   // D tiles ahead: at step i the loads of tile i + D go into the buffer of tile
   // i + D - 4 (the kernel's form is D = 2; D = 3 keeps a third tile in flight)
   if (loader) {
@@ -274,13 +295,20 @@ __global__ __launch_bounds__(512) void sched_rate(const char* src, int C, int sh
   for (int i = 0; i < 32; ++i) {
     const uint64_t t0 = __builtin_amdgcn_s_memtime();
     if (loader) {
-      if (i + D < 32) issue(i + D);
+      if (i + D < 32) {
+        issue(i + D);
+        if constexpr (PF > 0) prefetch(i + D + PF);
+      }
       const uint64_t t1 = __builtin_amdgcn_s_memtime();
       issued += t1 - t0;
       while (__builtin_amdgcn_s_memtime() - t1 < static_cast<uint64_t>(C)) {
       }
-      if (i + D < 32) wait_vm<9 * (D - 1)>();
-      else if (D == 3 && i + 2 < 32) wait_vm<9>();
+      // loads younger than tile i + 1 that may stay in flight (a prefetch follows each
+      // tile's loads)
+      constexpr int P = PF > 0 ? 1 : 0;
+      if (i + D < 32) wait_vm<9 * (D - 1) + P * D>();
+      else if (D == 3 && i + 2 < 32) wait_vm<9 + P * 2>();
+      else if (i + 1 < 32 && P) wait_vm<P * (D - 1)>();
       else wait_vm<0>();
     }
     __syncthreads();
@@ -392,7 +420,7 @@ static void run_stream(const char* src) {
   CHECK(hipEventDestroy(e1));
 }
 
-static void run_sched(const char* src, int64_t copy, int share, int C, int rot = 0, int D = 2) {
+static void run_sched(const char* src, int64_t copy, int share, int C, int rot = 0, int D = 2, int PF = 0) {
   uint64_t* rec;
   CHECK(hipMalloc(&rec, kBlocks * 16));
   hipEvent_t e0, e1;
@@ -405,8 +433,11 @@ static void run_sched(const char* src, int64_t copy, int share, int C, int rot =
     // per launch, two pairs in turn (the buffer holds four)
     const char* base = src + (share ? (rep % 3) * copy : (rep % 2) * 2 * copy);
     CHECK(hipEventRecord(e0));
-    if (D == 3) sched_rate<3><<<kBlocks, 512>>>(base, C, share, rot, rec);
-    else sched_rate<2><<<kBlocks, 512>>>(base, C, share, rot, rec);
+    if (D == 3) sched_rate<3, 0><<<kBlocks, 512>>>(base, C, share, rot, rec);
+    else if (PF == 1) sched_rate<2, 1><<<kBlocks, 512>>>(base, C, share, rot, rec);
+    else if (PF == 2) sched_rate<2, 2><<<kBlocks, 512>>>(base, C, share, rot, rec);
+    else if (PF == 4) sched_rate<2, 4><<<kBlocks, 512>>>(base, C, share, rot, rec);
+    else sched_rate<2, 0><<<kBlocks, 512>>>(base, C, share, rot, rec);
     CHECK(hipEventRecord(e1));
     CHECK(hipEventSynchronize(e1));
     float ms;
@@ -421,8 +452,8 @@ static void run_sched(const char* src, int64_t copy, int share, int C, int rot =
     is += static_cast<double>(h[2 * k + 1]);
   }
   const double us = tot / (reps - 3) * 1e3, bytes = (share ? 128.0 : 256.0) * kRangeBytes;
-  printf("sched    %s ranges, D=%d, C=%4d, rot %2d: %.1f us for %.0f MB (%.2f TB/s), step %.0f cycles, tile issue %.0f\n",
-         share ? "shared" : "distinct", D, C, rot, us, bytes / 1e6, bytes / (us * 1e-6) / 1e12, st / (kBlocks * 32.0),
+  printf("sched    %s ranges, D=%d, PF=%d, C=%4d, rot %2d: %.1f us for %.0f MB (%.2f TB/s), step %.0f cycles, tile issue %.0f\n",
+         share ? "shared" : "distinct", D, PF, C, rot, us, bytes / 1e6, bytes / (us * 1e-6) / 1e12, st / (kBlocks * 32.0),
          is / (kBlocks * 32.0));
   CHECK(hipEventDestroy(e0));
   CHECK(hipEventDestroy(e1));
@@ -470,6 +501,11 @@ int main(int argc, char** argv) {
   run_sched(src, copy, 1, 800, 0, 3);
   run_sched(src, copy, 1, 1400, 0, 3);
   run_sched(src, copy, 0, 800, 0, 3);
+  // an L2 prefetch of half of tile i + 2 + PF by each unit of the pair
+  for (int pf : {1, 2, 4}) {
+    run_sched(src, copy, 1, 0, 0, 2, pf);
+    run_sched(src, copy, 1, 800, 0, 2, pf);
+  }
   CHECK(hipFree(src));
   return 0;
 }
