@@ -152,13 +152,15 @@ def test_ragged_launches_fit_whole_waves():
     assert sum(cdiv(k, chunk) * 2 for k in host if k >= PRECISE_BELOW) <= 512
 
 
-def test_uniform_lengths_fill_one_wave():
-    """24 DeepSeek-shaped sequences (48 head-group units): five ranges each (240
-    workgroups), not six (288, a second wave for 32)."""
-    st, n = call_decode(ds_dims(), batch=24)
-    exp, chunk, cap = expected_workspace(h=128, n_q=1, batch=24, L=4097)
+@pytest.mark.parametrize("batch, ranges, chunk_tokens", [(24, 5, 832), (40, 3, 1376), (32, 4, 1056)])
+def test_uniform_lengths_fill_one_wave(batch, ranges, chunk_tokens):
+    """DeepSeek-shaped batches of 2 x batch head-group units: floor(256 / units)
+    ranges per sequence, so the launch fits one wave of the chip (24 sequences: five
+    ranges, 240 workgroups, not six and 288; 40 sequences: three, not four and 320)."""
+    st, n = call_decode(ds_dims(), batch=batch)
+    exp, chunk, cap = expected_workspace(h=128, n_q=1, batch=batch, L=4097)
     assert st == mla.MLA_OK and n == exp
-    assert cap == 24 * 5 and chunk == 832
+    assert cap == batch * ranges and chunk == chunk_tokens and 2 * cap <= 256
 
 
 def test_workspace_query_deepseek_shape():

@@ -553,6 +553,24 @@ def test_lengths_around_the_precise_threshold():
         assert np.max(np.abs(step.lse.cpu().numpy() - lse)) <= 1e-2
 
 
+@pytest.mark.parametrize("batch, ranges", [(24, 5), (40, 3)])
+def test_uniform_batches_that_do_not_divide_the_chip(batch, ranges):
+    """DeepSeek-shaped batches whose 64-row head groups (2 per sequence) do not divide
+    256: the planner gives each sequence floor(256 / units) ranges (24 sequences:
+    5 ranges, 240 workgroups; 40 sequences: 3 ranges, 240 workgroups), so the last
+    range is a remainder shorter than the others. Every output against the absorbed
+    twin, and sampled (sequence, head) pairs against the explicit form (the plan
+    itself is checked on the host by the workspace-query tests)."""
+    w = synth.make_workload(2, batch=batch)
+    say("case B=%d kv=%d" % (w.batch, int(w.kv_lens[0])))
+    t = synth.draw(w)
+    out = GpuStep(w, t).decode().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(out))
+    check_bf16(out, oracle_out(w, t, absorbed=True), what="B=%d, %d ranges (absorbed twin)" % (batch, ranges))
+    sel = [(0, 0), (batch // 2, 77), (batch - 1, 127)]
+    check_bf16(out, oracle_out(w, t, select=sel), mask=pair_mask(w, sel), what="B=%d sampled" % batch)
+
+
 def test_many_short_sequences():
     """64 sequences of 2..300 tokens, two queries each (all precise): every output."""
     w = synth.make_workload(4, batch=64, ctx_range=(0, 298))
