@@ -74,6 +74,22 @@ constexpr int kMaxRestarts = 8;
 
 __device__ __forceinline__ int swz(int t) { return (t >> 1) & 7; }
 
+// Tokens [t_begin, t_end) of range s of a kv-token sequence that the plan splits into
+// ns = ceil(kv / chunk) ranges. The sequence's nt = ceil(kv / kTileT) tiles are dealt
+// out evenly, range s taking tiles floor(s nt / ns) .. floor((s + 1) nt / ns) - 1:
+// the ranges of a sequence differ by at most one tile, none exceeds chunk tokens
+// (chunk is a multiple of kTileT, so nt <= ns chunk / kTileT), each holds at least
+// one tile (chunk >= kTileT, so ns <= nt), and the last ends at kv. With ranges of
+// chunk tokens and a remainder instead, 4097 tokens in four ranges would take 33,
+// 33, 33 and 30 tiles; dealt out they take 32, 32, 32 and 33, the last tile holding
+// one token.
+__device__ __forceinline__ void range_tokens(int s, int kv, int chunk, int& t_begin, int& t_end) {
+  const int ns = max(1, (kv + chunk - 1) / chunk);  // kv >= 1 for every listed pair
+  const int nt = max(1, (kv + kTileT - 1) / kTileT);
+  t_begin = kTileT * static_cast<int>(static_cast<int64_t>(s) * nt / ns);
+  t_end = min(kTileT * static_cast<int>(static_cast<int64_t>(s + 1) * nt / ns), kv);
+}
+
 template <int NW, int DR>
 struct Cfg {
   static constexpr int NBUF = 4;                           // tile buffers
@@ -216,8 +232,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const WorkItem item = a.list[pair];
   if (item.b < 0) return;  // uniform: past the pairs of this launch
   const int b = item.b, kv = item.kv;
-  const int t_begin = item.s * a.chunk;
-  const int t_end = min(t_begin + a.chunk, kv);
+  int t_begin, t_end;
+  range_tokens(item.s, kv, a.chunk, t_begin, t_end);
   if (t_begin >= t_end || kv < a.n_q) return;  // not listed by the plan
   const int n_tiles = (t_end - t_begin + kTileT - 1) / kTileT;
 
@@ -646,8 +662,8 @@ __global__ __launch_bounds__(256) void decode_roles_kernel(DecodeArgs a) {
   const WorkItem item = a.list[pair];
   if (item.b < 0) return;  // uniform: past the pairs of this launch
   const int b = item.b, kv = item.kv;
-  const int t_begin = item.s * a.chunk;
-  const int t_end = min(t_begin + a.chunk, kv);
+  int t_begin, t_end;
+  range_tokens(item.s, kv, a.chunk, t_begin, t_end);
   if (t_begin >= t_end || kv < a.n_q) return;  // not listed by the plan
   const int n_tiles = (t_end - t_begin + kTileT - 1) / kTileT;
 
@@ -1022,8 +1038,8 @@ __global__ __launch_bounds__(512) void decode_pp_kernel(DecodeArgs a) {
   const WorkItem item = a.list[pair];
   if (item.b < 0) return;  // uniform: past the pairs of this launch
   const int b = item.b, kv = item.kv;
-  const int t_begin = item.s * a.chunk;
-  const int t_end = min(t_begin + a.chunk, kv);
+  int t_begin, t_end;
+  range_tokens(item.s, kv, a.chunk, t_begin, t_end);
   if (t_begin >= t_end || kv < a.n_q) return;  // not listed by the plan
   const int n_tiles = (t_end - t_begin + kTileT - 1) / kTileT;
   const int bound = min(t_end - 1, kv - a.n_q);

@@ -27,7 +27,7 @@ hipError_t launch_append(int dtype, void* cache, const CacheRef& c, int batch, i
 // preparation writes the pairs of each class into a list on the device.
 struct WorkItem {
   int32_t b;   // sequence
-  int32_t s;   // token range [s * chunk, min((s + 1) * chunk, kv))
+  int32_t s;   // range s of the sequence's ceil(kv / chunk), its tiles dealt out evenly
   int32_t p;   // partial index: the range's partial rows are (p * n_q + j) * h + head
   int32_t kv;  // the sequence's length, clamped to max_kv_len
 };
