@@ -358,7 +358,9 @@ def summarize_append_counters(d):
     vals, cf, f_fac, w_fac = _counter_table(d, "pmc_append")
     per = {}
     for name in ("mla::splitk_gemm_kernel", "mla::latent_finish_kernel<unsigned short>"):
-        ks = [k for k in vals if k[0] == name]
+        # the product is a template over its staging depth (the append's one-chunk
+        # splits take splitk_gemm_kernel<1>)
+        ks = [k for k in vals if k[0] == name or k[0].startswith(name + "<")]
         if len(ks) != 1:
             raise SystemExit("%s not found once in the counter runs" % name)
         v = {c: sum(x) / len(x) for c, x in vals[ks[0]].items()}

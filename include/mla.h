@@ -74,7 +74,7 @@ typedef struct {
  * MLA_BF16: d_c = 512, d_rope in {0, 64}, d_qk_nope = 128, d_v = 128, n_heads a
  * multiple of 32 with n_heads * n_q a multiple of 64 (the DeepSeek-V2/V3 attention
  * shape and its position-free gated variant); with a gate, d_model a multiple of
- * 256. Paged caches need block_size a multiple of 32. Other shapes return
+ * 64. Paged caches need block_size a multiple of 32. Other shapes return
  * MLA_E_UNSUPPORTED (or MLA_E_SHAPE).
  *
  * Precision of the bf16 decode: the cache, weights and queries are bf16; products

@@ -24,7 +24,6 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kTile = 32;       // tokens per attention tile; split ranges are multiples of it
-constexpr int kGateSplit = 16;  // K-splits of the gate logits; must match the combine kernel
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 

@@ -18,7 +18,6 @@
 namespace mla {
 
 namespace {
-constexpr int kGateSplit = 16;            // K-splits of the gate GEMM
 constexpr int kWaves = 8;                 // waves per workgroup
 constexpr int kMaxRows = 16;              // query rows per workgroup
 constexpr int kAStride = 512 * 2 + 16;    // bytes per merged row in LDS (512 bf16, padded)

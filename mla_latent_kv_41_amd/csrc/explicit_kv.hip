@@ -22,7 +22,6 @@ constexpr int kHeadDim = 128;      // d_qk_nope = d_v
 constexpr int kTokPerWave = 32;    // expand: tokens per wave (one MFMA row block)
 constexpr int kTokPerWg = 128;     // expand: tokens per workgroup
 constexpr int kGroup = 8;          // decode: lanes per token (16 of the 128 dims each)
-constexpr int kGateSplit = 16;
 }  // namespace
 
 // W [d_c][h*128] (formula layout) -> MFMA B-operand fragments of the products

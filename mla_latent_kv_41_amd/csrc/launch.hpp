@@ -100,6 +100,10 @@ struct CombineArgs {
 hipError_t launch_combine_bf16(const CombineArgs& a, hipStream_t s);
 
 // g[ks][m][n] = Σ_{k in split ks} x[m][k] w[k][n]; K a multiple of 16 ksplit, N of 32
+// K splits of the gate logits g = x · W_G: the split-K product writes
+// [kGateSplit][M][h * 128] fp32 sums, which the combine kernels add in order
+constexpr int kGateSplit = 4;
+
 struct GemmArgs {
   const uint16_t* x;  // [M][K]
   const uint16_t* w;  // [K][N]

@@ -127,7 +127,7 @@ def expected_workspace(*, h, n_q, batch, L, d_rope=64, host=None, num_splits=0, 
     n = al(8) + al((batch + 1) * 4) + 2 * al((max(cap, 1) + 8) * 16) + q + (q if prec else 0)
     n += al(max(cap, 1) * n_q * h * 512 * 4) + al(max(cap, 1) * n_q * h * 8)
     if gated:
-        n += al(16 * M * h * 128 * 4)
+        n += al(4 * M * h * 128 * 4)  # four K splits of the gate logits
     if want_precise_chunk:
         return n, chunk, cap, chunk_p
     return n, chunk, cap

@@ -463,10 +463,11 @@ def test_fast_64_row_groups_forced_ranges():
         check_bf16(out, ref, what="h=64, %d ranges" % ns)
 
 
-@pytest.mark.parametrize("batch,d_model", [(40, 8192), (72, 4096), (3, 2048)])
+@pytest.mark.parametrize("batch,d_model", [(40, 8192), (72, 4096), (3, 2048), (3, 4160)])
 def test_gate_row_blocks_and_widths(batch, d_model):
-    """The gate GEMM over more than one 32-row block of queries, with K splits of 512
-    rows (two staged chunks), 256 rows or 128 rows (one partial chunk)."""
+    """The gate GEMM over more than one 32-row block of queries, with its four K
+    splits of 2048 rows (eight staged chunks, double-buffered), 1024, 512 (two) and
+    1040 rows (four chunks and a partial fifth)."""
     w = synth.make_workload(5, batch=batch, ctx=100)
     w.d_model = d_model
     t = synth.draw(w)
