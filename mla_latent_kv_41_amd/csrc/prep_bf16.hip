@@ -64,7 +64,9 @@ hipError_t launch_pack_bf16(const uint16_t* w_uk, const uint16_t* w_uv, uint16_t
 // consecutive blocks of one sequence; blocks of one query are consecutive.
 //
 // Precise mode (q_lo != nullptr): q_lo holds bf16(x - bf16(x)) of each scaled value
-// x, in the same order, so q_cat + q_lo carries about 16 significant bits of x.
+// x, in the same order, so q_cat + q_lo carries about 16 significant bits of x. Only
+// the rows of sequences the precise form takes (fewer than precise_below tokens)
+// are written; no other kernel reads q_lo.
 
 // Split plan of one decode call (see PlanArgs), built by one wave: lane l takes a
 // contiguous run of sequences, the wave scans the runs' totals, then every lane
@@ -152,6 +154,11 @@ __global__ __launch_bounds__(512) void qprep_kernel(QPrepArgs a) {
   const int i0 = kQHeads * g;
   const int nh = min(kQHeads, a.h - i0);  // heads in this group
   const bool lo_out = a.q_lo != nullptr;
+  // the low halves are read only by the precise form, which takes the sequences the
+  // plan puts in its list (the same rule as build_plan), so only their rows get them
+  auto precise_len = [&](int kv) __attribute__((always_inline)) {
+    return min(max(kv, 0), a.max_kv_len) < a.plan.precise_below;
+  };
 
   // query row m, head i -> offset of the block-order element (m, i, column 0)
   // (the column adds col_off(c))
@@ -165,10 +172,6 @@ __global__ __launch_bounds__(512) void qprep_kernel(QPrepArgs a) {
   if (w >= kQHeads) {
     // ================= side work: waves 4-7 =================
     const int sw = w - kQHeads;
-    // the plan goes to the side wave with the fewest rotation rows (wave 7 takes rows
-    // from t = 6 on, none when M <= 48), so no wave builds the plan and then waits on
-    // the loads of its rows
-    if (g == 0 && nb == 0 && sw == kQHeads - 1) build_plan(a.plan, l);
     const int srows = a.M > nb ? (a.M - nb + kQColBlocks - 1) / kQColBlocks : 0;
     // RoPE of q_R: half wave hf of wave sw takes side row t = 8u + 2sw + hf (u = 0, 1, ..),
     // query row m = nb + 8t. Pair k (columns 2k, 2k + 1) turns by pos * inv_freq[k], the
@@ -177,15 +180,31 @@ __global__ __launch_bounds__(512) void qprep_kernel(QPrepArgs a) {
     const int npair = a.d_r / 2, rchunks = a.d_r / 8;
     const int hf = l >> 5, hl = l & 31;
     const int hh = hl % kQHeads, ch = hl / kQHeads;
+    // the loads of a wave's next row are issued before its current row is rotated
+    auto side_loads = [&](int t_base, u32x4& x, int& kvl) __attribute__((always_inline)) {
+      const int t = t_base + hf;
+      const int m = nb + kQColBlocks * t;
+      x = u32x4{0u, 0u, 0u, 0u};
+      kvl = 0;
+      if (t < srows && ch < rchunks && hh < nh)
+        x = *reinterpret_cast<const u32x4*>(a.q_rope + (static_cast<int64_t>(m) * a.h + i0 + hh) * a.d_r + 8 * ch);
+      if (t < srows) kvl = a.kv_lens[m / a.n_q];
+    };
+    u32x4 x_next;
+    int kvl_next;
+    if (a.d_r > 0 && 2 * sw < srows) side_loads(2 * sw, x_next, kvl_next);
+    // the plan goes to the side wave with the fewest rotation rows (wave 7 takes rows
+    // from t = 6 on, none when M <= 48), after its first row's loads are issued, so
+    // no wave builds the plan and then waits on the loads of its rows
+    if (g == 0 && nb == 0 && sw == kQHeads - 1) build_plan(a.plan, l);
     for (int t_base = 2 * sw; a.d_r > 0 && t_base < srows; t_base += 2 * kQHeads) {  // uniform
       const int t = t_base + hf;
       const bool row_ok = t < srows;
       const int m = nb + kQColBlocks * t;
-      int kvl = 0;
-      u32x4 x = {0u, 0u, 0u, 0u};
       const bool item = row_ok && ch < rchunks && hh < nh;
-      if (item) x = *reinterpret_cast<const u32x4*>(a.q_rope + (static_cast<int64_t>(m) * a.h + i0 + hh) * a.d_r + 8 * ch);
-      if (row_ok) kvl = a.kv_lens[m / a.n_q];
+      const u32x4 x = x_next;
+      const int kvl = kvl_next;
+      if (t_base + 2 * kQHeads < srows) side_loads(t_base + 2 * kQHeads, x_next, kvl_next);
       float cs = 1.f, sn = 0.f;
       if (row_ok && hl < npair) {
         const double pos = static_cast<double>(min(kvl, a.max_kv_len) - a.n_q + m % a.n_q);
@@ -207,7 +226,7 @@ __global__ __launch_bounds__(512) void qprep_kernel(QPrepArgs a) {
       if (item) {
         const int64_t off = row_off(m, i0 + hh) + col_off(512 + 8 * ch);
         *reinterpret_cast<u32x4*>(a.q_cat + off) = o;
-        if (lo_out) *reinterpret_cast<u32x4*>(a.q_lo + off) = ol;
+        if (lo_out && precise_len(kvl)) *reinterpret_cast<u32x4*>(a.q_lo + off) = ol;
       }
     }
     return;
@@ -260,6 +279,16 @@ __global__ __launch_bounds__(512) void qprep_kernel(QPrepArgs a) {
   }
   __builtin_amdgcn_sched_barrier(0);  // every weight load issued before the rows' wait
   for (int mb = 0; mb * 32 < a.M; ++mb) {
+    // lengths of the sequences of this lane's stored rows, loaded ahead of the
+    // products (they decide which rows get low halves)
+    int kv_row[4] = {0, 0, 0, 0};
+    if (lo_out) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int m = 32 * mb + (l >> 3) + 8 * k;
+        if (m < a.M) kv_row[k] = a.kv_lens[m / a.n_q];
+      }
+    }
     f32x16 acc[2];
     if (given) {
       load_given(mb, acc);
@@ -307,9 +336,9 @@ __global__ __launch_bounds__(512) void qprep_kernel(QPrepArgs a) {
       const int r = (l >> 3) + 8 * k, m = 32 * mb + r;
       const u32x4 v = *(lds_u32x4*)(lds_ptr(area) + r * kQnB + cc * 16);
       if (m < a.M && w < nh) *reinterpret_cast<u32x4*>(a.q_cat + row_off(m, hw) + coff) = v;
-      if (lo_out) {
+      if (lo_out && m < a.M && w < nh && precise_len(kv_row[k])) {
         const u32x4 vl = *(lds_u32x4*)(lds_ptr(area) + r * kQnB + 128 + cc * 16);
-        if (m < a.M && w < nh) *reinterpret_cast<u32x4*>(a.q_lo + row_off(m, hw) + coff) = vl;
+        *reinterpret_cast<u32x4*>(a.q_lo + row_off(m, hw) + coff) = vl;
       }
     }
   }
