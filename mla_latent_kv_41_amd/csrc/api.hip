@@ -67,7 +67,7 @@ size_t elem_bytes(int dtype) { return dtype == MLA_F32 ? 4 : 2; }
 constexpr int kPreciseBelow = 4096;
 constexpr int kMaxSplitsPerSeq = 1024;  // bound on a sequence's token ranges
 constexpr int kMinRaggedChunk = 256;   // tokens per range at least, ragged batches
-constexpr int kRaggedPerSlot = 2;      // ragged batches: workgroups per CU slot
+constexpr int kRaggedPerSlot = 1;      // ragged batches: workgroups per CU slot
 constexpr int kRowsRangeMin = 1024;     // see the fast form's choice below
 #ifndef MLA_FAST64_FORM
 #define MLA_FAST64_FORM kFormPingPong
@@ -172,11 +172,12 @@ Plan plan_bf16(const Resolved& r, const mla_decode_args* a) {
   if (a->num_splits > 0) {
     chunk = ceil_div(L, a->num_splits);
   } else if (ragged) {
-    // ranges sized so the batch yields about two workgroups per slot: more ranges
-    // balance the lengths better, but every range writes fp32 partial rows that the
-    // combine reads back (measured on the ragged two-query workload, step 407 us at
-    // two per slot against 447 at three and 471 at four), at least kMinRaggedChunk
-    // tokens, so the partials of a range stay well below the cache bytes it reads
+    // ranges sized so the batch yields about one workgroup per slot, fitted below to
+    // one whole wave: more ranges balance the lengths better, but every range writes
+    // fp32 partial rows that the combine reads back (on the ragged two-query workload
+    // two per slot make the attention 8 us shorter and the combine 13 us longer), at
+    // least kMinRaggedChunk tokens, so the partials of a range stay well below the
+    // cache bytes it reads
     chunk = std::max<int64_t>(kMinRaggedChunk, ceil_div(total_units, kRaggedPerSlot * target));
   } else {
     // at most one workgroup per slot when every sequence is as long as the longest:

@@ -56,6 +56,7 @@ def call_decode(d, *, batch=32, n_q=1, max_kv_len=4097, t_max=4097, host=None, n
 
 PRECISE_BELOW = 4096   # sequences shorter than this take the precise attention form
 ALIGN = 256
+SLOT = 1               # ragged batches: fast-form workgroups per CU slot
 
 
 def cdiv(x, y):
@@ -104,13 +105,13 @@ def expected_workspace(*, h, n_q, batch, L, d_rope=64, host=None, num_splits=0, 
     if num_splits:
         chunk = cdiv(L, num_splits)
     elif ragged:
-        chunk = max(256, cdiv(units, 2 * 256))
+        chunk = max(256, cdiv(units, SLOT * 256))
     else:
         chunk = cdiv(L, min(max(1, 256 // (batch * groups(L))), cdiv(L, 32)))
     chunk = max(chunk, cdiv(L, 1024))
     chunk = min(cdiv(chunk, 32) * 32, top)
     if ragged and not num_splits:
-        chunk = fit(chunk, 2 * 256, 0 if own_prec else 2)
+        chunk = fit(chunk, SLOT * 256, 0 if own_prec else 2)
     chunk_p = chunk
     if own_prec:
         chunk_p = fit(min(cdiv(max(256, cdiv(pu, 256)), 32) * 32, top), 256, 1)
@@ -136,7 +137,8 @@ def expected_workspace(*, h, n_q, batch, L, d_rope=64, host=None, num_splits=0, 
 def test_ragged_launches_fit_whole_waves():
     """The ragged two-query workload's lengths: the precise launch's ranges grow from
     448 to 512 tokens so its 248 workgroups run as one wave of the chip (448-token
-    ranges give 276, a second wave for 20); the fast launch stays within two waves."""
+    ranges give 276, a second wave for 20); the fast launch's 4704-token ranges give
+    exactly one wave, 256 workgroups."""
     from mla_latent_kv_41_amd import synth
     w = synth.make_workload(4)
     host = [int(k) for k in w.kv_lens]
@@ -146,10 +148,10 @@ def test_ragged_launches_fit_whole_waves():
     exp, chunk, cap, chunk_p = expected_workspace(h=128, n_q=2, batch=w.batch, L=L, host=host,
                                                   want_precise_chunk=True)
     assert n == exp
-    assert chunk_p == 512
+    assert chunk_p == 512 and chunk == 4704
     short = [k for k in host if k < PRECISE_BELOW]
     assert sum(cdiv(k, chunk_p) * 4 for k in short) <= 256 < sum(cdiv(k, 448) * 4 for k in short)
-    assert sum(cdiv(k, chunk) * 2 for k in host if k >= PRECISE_BELOW) <= 512
+    assert sum(cdiv(k, chunk) * 2 for k in host if k >= PRECISE_BELOW) == 256
 
 
 @pytest.mark.parametrize("batch, ranges, chunk_tokens", [(24, 5, 832), (40, 3, 1376), (32, 4, 1056)])
