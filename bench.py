@@ -551,7 +551,7 @@ def summarize_traffic(d, cfg):
 
 
 
-ATTENTION_KERNELS = ("mla::decode_kernel", "mla::decode_roles_kernel", "mla::decode_pp_kernel")
+ATTENTION_KERNELS = ("mla::decode_kernel", "mla::decode_roles_kernel", "mla::decode_pp_kernel", "mla::decode_mixed_kernel")
 # Kernel-efficiency counter passes (one run each; rocprofv3 does not split counters
 # over passes): MFMA busy share, MFMA work, LDS busy share and bank conflicts; L2.
 EFF_PASSES = {"sq": "MfmaUtil LdsUtil LdsBankConflict SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE",

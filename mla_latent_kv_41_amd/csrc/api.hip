@@ -412,20 +412,32 @@ mla_status decode_impl(const mla_dims* dims, const CacheRef& cache, const mla_de
   d.d_r = r.d_r;
   d.chunk = p.chunk;
   const bool two = fast_units > 0 && prec_units > 0;
-  if (fast_units > 0) {
+  if (two && p.fast_form == kForm128 && fast_units % 8 == 0) {
+    // both forms in one grid (their block shapes agree): the precise units fill
+    // the CUs that the shorter fast ranges leave first, rather than waiting for the
+    // longest of them
     d.list = fast_list;
     d.form = p.fast_form;
     d.units = static_cast<int32_t>(fast_units);
-    if (launch_decode_bf16(d, stream, a->ev_attn_begin, two ? nullptr : a->ev_attn_end) != hipSuccess)
+    if (launch_decode_mixed_bf16(d, prec_list, p.chunk_precise, static_cast<int32_t>(prec_units), stream,
+                                 a->ev_attn_begin, a->ev_attn_end) != hipSuccess)
       return MLA_E_HIP;
-  }
-  if (prec_units > 0) {
-    d.list = prec_list;
-    d.chunk = p.chunk_precise;
-    d.form = kFormPrecise;
-    d.units = static_cast<int32_t>(prec_units);
-    if (launch_decode_bf16(d, stream, two ? nullptr : a->ev_attn_begin, a->ev_attn_end) != hipSuccess)
-      return MLA_E_HIP;
+  } else {
+    if (fast_units > 0) {
+      d.list = fast_list;
+      d.form = p.fast_form;
+      d.units = static_cast<int32_t>(fast_units);
+      if (launch_decode_bf16(d, stream, a->ev_attn_begin, two ? nullptr : a->ev_attn_end) != hipSuccess)
+        return MLA_E_HIP;
+    }
+    if (prec_units > 0) {
+      d.list = prec_list;
+      d.chunk = p.chunk_precise;
+      d.form = kFormPrecise;
+      d.units = static_cast<int32_t>(prec_units);
+      if (launch_decode_bf16(d, stream, two ? nullptr : a->ev_attn_begin, a->ev_attn_end) != hipSuccess)
+        return MLA_E_HIP;
+    }
   }
 
   CombineArgs c{};

@@ -74,6 +74,20 @@ constexpr int kMaxRestarts = 8;
 
 __device__ __forceinline__ int swz(int t) { return (t >> 1) & 7; }
 
+// LDS of the 128-row and role-split forms: four tile buffers of kTileT rows of 576
+// bf16 and the P buffers, 160 KiB in all. Declared once at file scope, so a launch
+// that runs either form in its workgroups (decode_mixed_kernel) holds one set. Tile
+// buffers as distinct arrays: reads of one are provably independent of the
+// direct-to-LDS loads landing in another, so they need no load wait.
+constexpr int kLdsTileBytes = kTileT * (512 + 64) * 2;
+constexpr int kLdsPBytes = 16 * 1024;
+__shared__ __attribute__((aligned(1024))) char lds_tile0[kLdsTileBytes];
+__shared__ __attribute__((aligned(1024))) char lds_tile1[kLdsTileBytes];
+__shared__ __attribute__((aligned(1024))) char lds_tile2[kLdsTileBytes];
+__shared__ __attribute__((aligned(1024))) char lds_tile3[kLdsTileBytes];
+__shared__ __attribute__((aligned(16))) char lds_p[kLdsPBytes];
+static_assert(4 * kLdsTileBytes + kLdsPBytes <= 160 * 1024, "LDS");
+
 // Tokens [t_begin, t_end) of range s of a kv-token sequence that the plan splits into
 // ns = ceil(kv / chunk) ranges. The sequence's nt = ceil(kv / kTileT) tiles are dealt
 // out evenly, range s taking tiles floor(s nt / ns) .. floor((s + 1) nt / ns) - 1:
@@ -201,21 +215,20 @@ __device__ __forceinline__ void mfma_va_last(f32x16& c, const u32x4& a, const u3
 
 }  // namespace
 
+// The 128-row form's work for workgroup bid of its launch.
 template <int NW, int DR>
-__global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_128(const DecodeArgs& a, const int bid) {
   using C = Cfg<NW, DR>;
   constexpr int NBUF = C::NBUF, CBW = C::CBW, RB = C::RB;
-  // Tile buffers as distinct arrays: reads of one are provably independent of the
-  // direct-to-LDS loads landing in another, so they need no load wait.
-  __shared__ __attribute__((aligned(1024))) char s_tile0[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char s_tile1[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char s_tile2[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char s_tile3[C::TILE_BYTES];
+  char* const s_tile0 = lds_tile0;
+  char* const s_tile1 = lds_tile1;
+  char* const s_tile2 = lds_tile2;
+  char* const s_tile3 = lds_tile3;
   // P fragments [parity][row block][k-step][lane]: P of tile i goes into buffer i % 2,
   // so publishing it never waits for readers of tile i - 1's P.
   constexpr int PBUF = RB * 2 * 1024;
-  __shared__ __attribute__((aligned(16))) char s_p[2 * PBUF];
-  static_assert(4 * C::TILE_BYTES + 2 * PBUF <= 160 * 1024, "LDS");
+  char* const s_p = lds_p;
+  static_assert(C::TILE_BYTES <= kLdsTileBytes && 2 * PBUF <= kLdsPBytes, "LDS");
 
   const int tid = threadIdx.x, l = tid % 64;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64);  // wave index, uniform
@@ -224,8 +237,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 
   // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous
   // range of units so one sequence's splits (and head groups) share an L2.
-  int u = blockIdx.x;
-  if ((a.units & 7) == 0) u = (blockIdx.x & 7) * (a.units >> 3) + (blockIdx.x >> 3);
+  int u = bid;
+  if ((a.units & 7) == 0) u = (bid & 7) * (a.units >> 3) + (bid >> 3);
   StampRec stamp;
   if constexpr (kStamps) stamp.begin();
   const int pair = u / hgroups, hg = u - pair * hgroups;
@@ -606,6 +619,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   if constexpr (kStamps) stamp.end(a.stamps, u, w, l);
 }
 
+template <int NW, int DR>
+__global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
+  decode_128<NW, DR>(a, blockIdx.x);
+}
+
 // Role-split form for 64 query rows per workgroup (a (sequence, token range, head
 // group) unit of two 32-row query blocks). Waves 0-1 own the scores and the softmax
 // of block w (its Q_cat fragments in VGPRs). Waves 2-3 own the value contraction for
@@ -631,7 +649,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 // This form serves the sequences too short for bf16 rounding of the query and of
 // P to average out (the host plan sends them here).
 template <int DR, bool PRECISE>
-__global__ __launch_bounds__(256) void decode_roles_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_roles(const DecodeArgs& a, const int bid) {
   constexpr int ROW = 512 + DR, ROWB = ROW * 2, CH = ROW / 8, KS = ROW / 16;
   constexpr int R = 64;                           // query rows per workgroup
   constexpr int TILE_BYTES = kTileT * ROWB;
@@ -639,14 +657,14 @@ __global__ __launch_bounds__(256) void decode_roles_kernel(DecodeArgs a) {
   constexpr int CBW = 8;                          // value column blocks per value wave
   constexpr int RB = 2;                           // row blocks of 32 query rows
   static_assert((kTileT * CH) % 128 == 0, "tile loads per value wave");
-  __shared__ __attribute__((aligned(1024))) char s_tile0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char s_tile1[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char s_tile2[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char s_tile3[TILE_BYTES];
+  char* const s_tile0 = lds_tile0;
+  char* const s_tile1 = lds_tile1;
+  char* const s_tile2 = lds_tile2;
+  char* const s_tile3 = lds_tile3;
   constexpr int PBUF = RB * 2 * 1024;  // P fragments [row block][k-step][lane]
   // [parity] high P, then (PRECISE) [parity] low P
-  __shared__ __attribute__((aligned(16))) char s_p[(PRECISE ? 4 : 2) * PBUF];
-  static_assert(4 * TILE_BYTES + (PRECISE ? 4 : 2) * PBUF <= 160 * 1024, "LDS");
+  char* const s_p = lds_p;
+  static_assert(TILE_BYTES <= kLdsTileBytes && (PRECISE ? 4 : 2) * PBUF <= kLdsPBytes, "LDS");
 
   const int tid = threadIdx.x, l = tid % 64;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64);  // wave index, uniform
@@ -654,8 +672,8 @@ __global__ __launch_bounds__(256) void decode_roles_kernel(DecodeArgs a) {
   const int vw = w - 2;  // value wave index (value waves only)
   const int hgroups = (a.h * a.n_q) / R;
   const int HB = a.h / 32;
-  int u = blockIdx.x;
-  if ((a.units & 7) == 0) u = (blockIdx.x & 7) * (a.units >> 3) + (blockIdx.x >> 3);
+  int u = bid;
+  if ((a.units & 7) == 0) u = (bid & 7) * (a.units >> 3) + (bid >> 3);
   StampRec stamp;
   if constexpr (kStamps) stamp.begin();
   const int pair = u / hgroups, hg = u - pair * hgroups;
@@ -978,6 +996,35 @@ __global__ __launch_bounds__(256) void decode_roles_kernel(DecodeArgs a) {
   if (scorer) run(Ic<1>{});
   else run(Ic<0>{});
   if constexpr (kStamps) stamp.end(a.stamps, u, w, l);
+}
+
+template <int DR, bool PRECISE>
+__global__ __launch_bounds__(256) void decode_roles_kernel(DecodeArgs a) {
+  decode_roles<DR, PRECISE>(a, blockIdx.x);
+}
+
+// The fast and the precise launch of one decode call as one grid: workgroups below
+// fast.units take the 128-row form's units, the rest the precise form's. Workgroups
+// are dispatched in order, so every fast unit is placed first and each precise one
+// starts on the first CU a fast unit leaves, filling the idle end of a launch whose
+// ranges differ in length (ragged batches). fast.units is a multiple of 8, so each
+// part keeps its own XCD-contiguous order. Both forms take the whole of a CU's LDS.
+// The precise part differs from the fast one only in its list, range length and
+// unit count.
+template <int DR>
+__global__ __launch_bounds__(256) void decode_mixed_kernel(DecodeArgs fast, const WorkItem* prec_list,
+                                                           int prec_chunk, int prec_units) {
+  const int bid = blockIdx.x;
+  if (bid < fast.units) {
+    decode_128<4, DR>(fast, bid);
+  } else {
+    DecodeArgs prec = fast;
+    prec.list = prec_list;
+    prec.chunk = prec_chunk;
+    prec.units = prec_units;
+    prec.form = kFormPrecise;
+    decode_roles<DR, true>(prec, bid - fast.units);
+  }
 }
 
 // Eight-wave form for 64 query rows per workgroup (the unit of the role-split form:
@@ -1415,6 +1462,22 @@ hipError_t launch_decode_bf16(const DecodeArgs& a_in, hipStream_t s, hipEvent_t 
   } else {
     return hipErrorInvalidValue;
   }
+#undef MLA_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_mixed_bf16(const DecodeArgs& fast, const WorkItem* prec_list, int prec_chunk,
+                                    int prec_units, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+  if (fast.form != kForm128 || fast.q_lo == nullptr || prec_list == nullptr) return hipErrorInvalidValue;
+  if ((fast.h * fast.n_q) % 128 != 0 || fast.h % 32 != 0) return hipErrorInvalidValue;
+  if (fast.units <= 0 || fast.units % 8 != 0 || prec_units <= 0 || prec_chunk <= 0 ||
+      static_cast<int64_t>(fast.units) + prec_units > INT32_MAX)
+    return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(fast.units + prec_units));
+#define MLA_LAUNCH(K) hipExtLaunchKernelGGL(K, grid, dim3(256), 0, s, ev0, ev1, 0, fast, prec_list, prec_chunk, prec_units)
+  if (fast.d_r == 64) MLA_LAUNCH(decode_mixed_kernel<64>);
+  else if (fast.d_r == 0) MLA_LAUNCH(decode_mixed_kernel<0>);
+  else return hipErrorInvalidValue;
 #undef MLA_LAUNCH
   return hipGetLastError();
 }

@@ -84,6 +84,11 @@ struct DecodeArgs {
   uint64_t* stamps;        // instrumented builds: the phase stamp buffer (set by the launcher)
 };
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+// One grid for a call's fast launch (fast: kForm128, units a multiple of 8, q_lo
+// set) and its precise launch, whose arguments are fast's but for the
+// list, range length and unit count given: the fast units first.
+hipError_t launch_decode_mixed_bf16(const DecodeArgs& fast, const WorkItem* prec_list, int prec_chunk,
+                                    int prec_units, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 
 struct CombineArgs {
   const float* o_part;      // [pairs][n_q][h][512]

@@ -463,6 +463,30 @@ def test_fast_64_row_groups_forced_ranges():
         check_bf16(out, ref, what="h=64, %d ranges" % ns)
 
 
+@pytest.mark.parametrize("cid", [4, 5])
+def test_fast_and_precise_forms_in_one_grid(cid):
+    """Sequences on both sides of 4096 tokens with 128-row fast groups (two queries,
+    token ranges forced to 4 per sequence): the fast and the precise units run in one
+    launch, the fast ones first (a multiple of 8 of them). With the RoPE key (paged,
+    lengths 1606 to 5916) and without it (the gated shape, 64 heads, lengths 900 to
+    4801): every output and lse."""
+    if cid == 4:
+        w = synth.make_workload(4, batch=4, ctx_range=(1000, 6000))
+    else:
+        w = synth.make_workload(5, batch=4, ctx=4800)
+        w.n_q = 2
+        w.kv_lens = np.array([4801, 900, 4500, 2000], np.int32)
+    long = int(np.sum(w.kv_lens >= 4096))
+    assert 0 < long < w.batch and long * 4 * (w.h * w.n_q // 128) % 8 == 0
+    say("case %d h=%d B=%d n_q=%d kv=%s" % (cid, w.h, w.batch, w.n_q, list(w.kv_lens)))
+    t = synth.draw(w)
+    step = GpuStep(w, t)
+    out = step.decode(num_splits=4).cpu().numpy().astype(np.float64)
+    ref, lse = oracle_out(w, t, want_lse=True)
+    check_bf16(out, ref, what="case %d, both forms in one grid" % cid)
+    assert np.max(np.abs(step.lse.cpu().numpy() - lse)) <= 1e-2
+
+
 @pytest.mark.parametrize("batch,d_model", [(40, 8192), (72, 4096), (3, 2048), (3, 4160)])
 def test_gate_row_blocks_and_widths(batch, d_model):
     """The gate GEMM over more than one 32-row block of queries, with its four K
