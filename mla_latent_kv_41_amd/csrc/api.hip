@@ -82,7 +82,7 @@ struct Plan {
   int chunk_precise; // ... of the precise form's sequences
   int64_t cap;       // pairs the workspace holds: a bound on Σ_b ceil(kv_b / chunk)
   int64_t fast_pairs, prec_pairs;  // bounds on the pairs of each list (0: not launched)
-  int comb_rows;     // combine: query rows per workgroup (16, 8, 4, 2 or 1)
+  int comb_rows;     // combine: query rows per workgroup (32, 16, 8, 4, 2 or 1)
 };
 
 int64_t ceil_div(int64_t x, int64_t y) { return (x + y - 1) / y; }
@@ -212,10 +212,10 @@ Plan plan_bf16(const Resolved& r, const mla_decode_args* a) {
     p.fast_pairs = L >= kPreciseBelow ? p.cap : 0;
     p.prec_pairs = p.cap;
   }
-  // combine grid: (h, M / rows), rows 16, 8, 4, 2 or 1: halved until the grid has a
+  // combine grid: (h, M / rows), rows 32, 16, 8, 4, 2 or 1: halved until the grid has a
   // workgroup per CU
   const int M = a->batch * a->n_q;
-  p.comb_rows = 16;
+  p.comb_rows = 32;
   while (p.comb_rows > 1 && static_cast<int64_t>(r.h) * ceil_div(M, p.comb_rows) < target) p.comb_rows /= 2;
   return p;
 }

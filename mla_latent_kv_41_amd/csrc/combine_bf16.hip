@@ -19,7 +19,6 @@ namespace mla {
 
 namespace {
 constexpr int kWaves = 8;                 // waves per workgroup
-constexpr int kMaxRows = 16;              // query rows per workgroup
 constexpr int kAStride = 512 * 2 + 16;    // bytes per merged row in LDS (512 bf16, padded)
 
 template <int N>
@@ -43,7 +42,7 @@ __device__ __forceinline__ void to_bf16_pair(const float (&x)[N], uint32_t (&hi)
 }
 }  // namespace
 
-// grid (h, ceil(M / R)), 512 threads; R = rows_per_wg in {16, 8, 4, 2, 1} query rows.
+// grid (h, ceil(M / R)), 512 threads; R = rows_per_wg in {32, 16, 8, 4, 2, 1} query rows.
 // Workgroup (i, mb) merges query rows m0 .. m0 + R - 1 of head i over all 512 latent
 // columns and writes their up-projection
 //   out[m][i*128 + d] = Σ_c o_lat[m][i][c] · W_UV_i[c][d]
@@ -51,8 +50,8 @@ __device__ __forceinline__ void to_bf16_pair(const float (&x)[N], uint32_t (&hi)
 // clearing and the result does not depend on timing.
 //
 // Merge. The statistics of a row are formed by whole waves: WPR = 8 / R waves share
-// a row when R < 8, each taking 512 / WPR columns (VW = 8 / WPR per lane); with R = 8
-// or 16 each wave takes one or two rows (columns 8l .. 8l + 7 per lane). Sequence b's
+// a row when R < 8, each taking 512 / WPR columns (VW = 8 / WPR per lane); with R = 8,
+// 16 or 32 each wave takes one, two or four rows (columns 8l .. 8l + 7 per lane). Sequence b's
 // ranges hold partial indices seq_off[b] .. seq_off[b + 1] - 1. Lane s reads range
 // s's (m, l) (ranges past 64 in a loop), wave reductions give M and L, lane s forms
 // the weight 2^(m_s - M) / L, and the merge reads the weights back with readlane.
@@ -60,17 +59,21 @@ __device__ __forceinline__ void to_bf16_pair(const float (&x)[N], uint32_t (&hi)
 // ranges merge in a fixed order.
 //
 // Up-projection, on v_mfma_f32_16x16x32_bf16: the merged rows enter as hi + lo pairs
-// of bf16 rows from LDS (rows past the workgroup's read as zeros). Wave w computes the
-// 16 output columns of block w over all 512 latent columns (its 16 W_UV_i fragments
-// are loaded first), applies the gate and stores.
+// of bf16 rows from LDS (rows past the workgroup's read as zeros), 16 rows per MFMA
+// block. Wave w computes the 16 output columns of block w over all 512 latent columns
+// (its 16 W_UV_i fragments are loaded first), applies the gate and stores. Every
+// workgroup reads all of W_UV_i (128 KiB), so more rows per workgroup read it fewer
+// times: a batch of many query rows takes 32.
 template <int WPR, int RPW>
 __global__ __launch_bounds__(kWaves * 64) void combine_kernel(CombineArgs a) {
   constexpr int VW = 8 / WPR;              // floats per lane of a row
-  static_assert(RPW == 1 || WPR == 1, "two rows per wave only with whole rows");
+  static_assert(RPW == 1 || WPR == 1, "several rows per wave only with whole rows");
   constexpr int NB = WPR == 1 ? 4 : 8;     // partial rows per row in flight
+  constexpr int kRows = WPR == 1 ? kWaves * RPW : kWaves / WPR;  // query rows per workgroup
+  constexpr int NRB = (kRows + 15) / 16;                          // 16-row MFMA blocks
   using V = typename VecT<VW>::T;
-  __shared__ __attribute__((aligned(16))) char s_hi[kMaxRows * kAStride];
-  __shared__ __attribute__((aligned(16))) char s_lo[kMaxRows * kAStride];
+  __shared__ __attribute__((aligned(16))) char s_hi[kRows * kAStride];
+  __shared__ __attribute__((aligned(16))) char s_lo[kRows * kAStride];
   const int i = blockIdx.x, mb = blockIdx.y;
   const int tid = threadIdx.x, l = tid % 64;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -181,31 +184,37 @@ __global__ __launch_bounds__(kWaves * 64) void combine_kernel(CombineArgs a) {
   __syncthreads();
 
   // ---- (o_hi + o_lo)[rows][:] · W_UV_i[:][16 w + ..]; A row l%16 (zero past the
-  //      workgroup's rows), k = 32 ks + 8 (l/16) + e; the hi and lo products run as
-  //      two accumulation chains, added at the end
-  f32x4 acc_h = {}, acc_l = {};
-  const int ar = l & 15;
-  const bool arow = ar < rows;
-  const int aoff = ar * kAStride + (l >> 4) * 16;
+  //      workgroup's rows), row 16 rb + l%16 of block rb, k = 32 ks + 8 (l/16) + e;
+  //      the hi and lo products run as two accumulation chains, added at the end
+  f32x4 acc_h[NRB], acc_l[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) acc_h[rb] = acc_l[rb] = f32x4{};
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks) {
-    u32x4 ah = {0u, 0u, 0u, 0u}, al = {0u, 0u, 0u, 0u};
-    if (arow) {
-      ah = *(lds_u32x4*)(lds_ptr(s_hi) + aoff + ks * 64);
-      al = *(lds_u32x4*)(lds_ptr(s_lo) + aoff + ks * 64);
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int ar = 16 * rb + (l & 15);
+      const int aoff = ar * kAStride + (l >> 4) * 16 + ks * 64;
+      u32x4 ah = {0u, 0u, 0u, 0u}, al = {0u, 0u, 0u, 0u};
+      if (ar < rows) {
+        ah = *(lds_u32x4*)(lds_ptr(s_hi) + aoff);
+        al = *(lds_u32x4*)(lds_ptr(s_lo) + aoff);
+      }
+      acc_h[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah), as_bf16x8(bfr[ks]), acc_h[rb], 0, 0, 0);
+      acc_l[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al), as_bf16x8(bfr[ks]), acc_l[rb], 0, 0, 0);
     }
-    acc_h = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah), as_bf16x8(bfr[ks]), acc_h, 0, 0, 0);
-    acc_l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al), as_bf16x8(bfr[ks]), acc_l, 0, 0, 0);
   }
-  // D lane l: output column 16 w + l % 16, rows 4 (l / 16) + v
+  // D lane l: output column 16 w + l % 16, rows 16 rb + 4 (l / 16) + v
   const int width = a.h * 128;
   const int col = i * 128 + 16 * w + (l & 15);
 #pragma unroll
+  for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const int r = 4 * (l >> 4) + v;
+    const int r = 16 * rb + 4 * (l >> 4) + v;
     if (r >= rows) continue;
     const int m = m0 + r;
-    float ov = acc_h[v] + acc_l[v];
+    float ov = acc_h[rb][v] + acc_l[rb][v];
     if (a.gate) {  // out = sigmoid(g) o
       float g = 0.f;
       for (int ks = 0; ks < kGateSplit; ++ks) g += a.gate[(static_cast<int64_t>(ks) * M + m) * width + col];
@@ -218,9 +227,10 @@ __global__ __launch_bounds__(kWaves * 64) void combine_kernel(CombineArgs a) {
 hipError_t launch_combine_bf16(const CombineArgs& a, hipStream_t s) {
   const int M = a.batch * a.n_q;
   const int R = a.rows_per_wg;
-  if (!(R == 16 || R == 8 || R == 4 || R == 2 || R == 1) || M <= 0) return hipErrorInvalidValue;
+  if (!(R == 32 || R == 16 || R == 8 || R == 4 || R == 2 || R == 1) || M <= 0) return hipErrorInvalidValue;
   const dim3 grid(a.h, (M + R - 1) / R);
-  if (R == 16) combine_kernel<1, 2><<<grid, kWaves * 64, 0, s>>>(a);
+  if (R == 32) combine_kernel<1, 4><<<grid, kWaves * 64, 0, s>>>(a);
+  else if (R == 16) combine_kernel<1, 2><<<grid, kWaves * 64, 0, s>>>(a);
   else if (R == 8) combine_kernel<1, 1><<<grid, kWaves * 64, 0, s>>>(a);
   else if (R == 4) combine_kernel<2, 1><<<grid, kWaves * 64, 0, s>>>(a);
   else if (R == 2) combine_kernel<4, 1><<<grid, kWaves * 64, 0, s>>>(a);

@@ -100,7 +100,7 @@ struct CombineArgs {
   float* o_lat;             // latent mode: [M][h][512] merged latent output (no W_UV), or nullptr
   float* lse;               // [M][h] or nullptr
   int32_t batch, n_q, h;
-  int32_t rows_per_wg;      // query rows per workgroup: 16, 8, 4, 2 or 1
+  int32_t rows_per_wg;      // query rows per workgroup: 32, 16, 8, 4, 2 or 1
 };
 hipError_t launch_combine_bf16(const CombineArgs& a, hipStream_t s);
 

@@ -200,7 +200,7 @@ def test_error_bound_holds_on_short_ragged_sequences():
 
 @pytest.mark.parametrize("cid,batch,splits,ctx", [(2, 40, 6, 900), (4, 20, 5, 900), (2, 72, 6, 200), (4, 36, 5, 200)])
 def test_combine_row_blocks_with_uneven_splits(cid, batch, splits, ctx):
-    """40 or 72 query rows: three or five 16-row combine blocks (the last holds 8).
+    """40 or 72 query rows: two or three 32-row combine blocks (the last holds 8).
     Lengths are spread so the rows of one block hold different numbers of splits, and
     the partials of splits past a row's last one are poisoned (NaN). Every output
     against 2e-2 x RMS and the first-order bf16 bound, and lse."""
